@@ -1,0 +1,224 @@
+"""Block-sparse video attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libvsa.so`` (declared in
+``include/vsa.h``).  Every computation runs in the library's HIP kernels; this
+module only allocates outputs and workspaces with PyTorch, passes raw device
+pointers and the current HIP stream, and turns status codes into exceptions.
+There is no CPU fallback: without the built library every call raises.
+
+Functions mirror the C entry points:
+    tile_permute, tile_unpermute, mask_nnz_bound, build_mask, attn_fwd
+plus ``attention``, which composes them into one block-sparse attention call.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvsa.so")
+
+LAYOUT_TOKEN_MAJOR = 0
+LAYOUT_FEATURE_MAJOR = 1
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "buffer too small",
+           4: "index overflow", 5: "HIP runtime error"}
+
+
+class VsaError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        super().__init__(f"{where}: {_STATUS.get(code, code)} ({detail})")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("W", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libvsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_attention_19_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SP = ctypes.POINTER(Shape)
+    sig = {
+        "vsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "vsa_last_error": (ctypes.c_char_p, []),
+        "vsa_num_tiles": (I32, [SP]),
+        "vsa_tile_permute": (ctypes.c_int, [SP, P, P, I32, P]),
+        "vsa_tile_unpermute": (ctypes.c_int, [SP, P, P, P]),
+        "vsa_mask_nnz_bound": (I64, [SP, I32, I32]),
+        "vsa_mask_workspace_bytes": (SZ, [SP]),
+        "vsa_build_mask": (ctypes.c_int, [SP, P, P, I32, I32, P, P, I64, P, P, SZ, P]),
+        "vsa_attn_workspace_bytes": (SZ, [SP, I32]),
+        "vsa_attn_fwd": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, I32, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(code: int, where: str) -> None:
+    if code != 0:
+        raise VsaError(code, where, lib().vsa_last_error().decode())
+
+
+def shape(batch: int, heads: int, head_dim: int, T: int, H: int, W: int) -> Shape:
+    return Shape(batch, heads, head_dim, T, H, W)
+
+
+def num_tiles(s: Shape) -> int:
+    n = lib().vsa_num_tiles(ctypes.byref(s))
+    if n < 0:
+        raise ValueError(f"invalid shape: {lib().vsa_last_error().decode()}")
+    return n
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.contiguous()
+
+
+def tile_permute(x: torch.Tensor, s: Shape, layout: int = LAYOUT_TOKEN_MAJOR,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [B, N, heads, D] raster -> tile-major (token- or feature-major tiles)."""
+    x = _require(x, torch.bfloat16, "x")
+    nT = num_tiles(s)
+    if layout == LAYOUT_TOKEN_MAJOR:
+        shp = (s.batch, s.heads, nT * 64, s.head_dim)
+    else:
+        shp = (s.batch, s.heads, nT, s.head_dim, 64)
+    if x.shape != (s.batch, s.T * s.H * s.W, s.heads, s.head_dim):
+        raise ValueError(f"x has shape {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty(shp, dtype=torch.bfloat16, device=x.device)
+    _check(lib().vsa_tile_permute(ctypes.byref(s), _ptr(x), _ptr(out), layout, _stream(x.device)),
+           "vsa_tile_permute")
+    return out
+
+
+def tile_unpermute(o_t: torch.Tensor, s: Shape, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [B, heads, nT*64, D] tile-major -> [B, N, heads, D] raster."""
+    o_t = _require(o_t, torch.bfloat16, "o_t")
+    if out is None:
+        out = torch.empty((s.batch, s.T * s.H * s.W, s.heads, s.head_dim), dtype=torch.bfloat16,
+                          device=o_t.device)
+    _check(lib().vsa_tile_unpermute(ctypes.byref(s), _ptr(o_t), _ptr(out), _stream(o_t.device)),
+           "vsa_tile_unpermute")
+    return out
+
+
+def mask_nnz_bound(s: Shape, r_max: int, dense_count: int) -> int:
+    n = lib().vsa_mask_nnz_bound(ctypes.byref(s), r_max, dense_count)
+    if n < 0:
+        raise ValueError("invalid shape, r_max or dense_count")
+    return n
+
+
+def build_mask(radii: torch.Tensor, scores: torch.Tensor, s: Shape, dense_count: int,
+               r_max: Optional[int] = None, with_routed: bool = True):
+    """uint8 radii / float32 scores [B, heads, nT] -> (row_ptr int32 [rows+1],
+    col_idx int32 [capacity], routed uint8 [B, heads, nT] or None).
+
+    ``r_max`` defaults to 255 (capacity for full rows)."""
+    radii = _require(radii, torch.uint8, "radii")
+    scores = _require(scores, torch.float32, "scores")
+    nT = num_tiles(s)
+    if radii.shape != (s.batch, s.heads, nT) or scores.shape != (s.batch, s.heads, nT):
+        raise ValueError("radii / scores must be [B, heads, nT]")
+    r_max = 255 if r_max is None else int(r_max)
+    cap = mask_nnz_bound(s, r_max, dense_count)
+    dev = radii.device
+    rows = s.batch * s.heads * nT
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    routed = torch.empty((s.batch, s.heads, nT), dtype=torch.uint8, device=dev) if with_routed else None
+    ws_bytes = lib().vsa_mask_workspace_bytes(ctypes.byref(s))
+    ws = None if with_routed else torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(lib().vsa_build_mask(ctypes.byref(s), _ptr(radii), _ptr(scores), dense_count, r_max,
+                                _ptr(row_ptr), _ptr(col_idx), cap, _ptr(routed), _ptr(ws),
+                                ws_bytes if ws is not None else 0, _stream(dev)),
+           "vsa_build_mask")
+    return row_ptr, col_idx, routed
+
+
+def attn_workspace_bytes(s: Shape, kv_chunk: int = 0) -> int:
+    return int(lib().vsa_attn_workspace_bytes(ctypes.byref(s), kv_chunk))
+
+
+def attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: torch.Tensor,
+             col_idx: torch.Tensor, s: Shape, scale: Optional[float] = None, kv_chunk: int = 0,
+             with_lse: bool = True, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Tile-major q/k [B, heads, nT*64, D], feature-major v [B, heads, nT, D, 64]
+    + CSR -> (o_t bf16 [B, heads, nT*64, D], lse float32 [B, heads, nT*64])."""
+    q_t = _require(q_t, torch.bfloat16, "q_t")
+    k_t = _require(k_t, torch.bfloat16, "k_t")
+    v_t = _require(v_t, torch.bfloat16, "v_t")
+    row_ptr = _require(row_ptr, torch.int32, "row_ptr")
+    col_idx = _require(col_idx, torch.int32, "col_idx")
+    nT = num_tiles(s)
+    D = s.head_dim
+    tok = (s.batch, s.heads, nT * 64, D)
+    if q_t.shape != tok or k_t.shape != tok or v_t.shape != (s.batch, s.heads, nT, D, 64):
+        raise ValueError("q_t / k_t / v_t shapes do not match the shape")
+    if row_ptr.numel() != s.batch * s.heads * nT + 1:
+        raise ValueError("row_ptr must have B*heads*nT + 1 entries")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q_t.device
+    if out is None:
+        out = torch.empty(tok, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(tok[:3], dtype=torch.float32, device=dev) if with_lse else None
+    ws_bytes = attn_workspace_bytes(s, kv_chunk)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(lib().vsa_attn_fwd(ctypes.byref(s), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(row_ptr),
+                              _ptr(col_idx), scale, _ptr(out), _ptr(lse), kv_chunk,
+                              _ptr(workspace), workspace.numel(), _stream(dev)),
+           "vsa_attn_fwd")
+    return out, lse
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Tuple[int, int, int],
+              radii: torch.Tensor, scores: torch.Tensor, dense_count: int,
+              scale: Optional[float] = None, r_max: Optional[int] = None,
+              kv_chunk: int = 0) -> torch.Tensor:
+    """Block-sparse attention of bf16 q, k, v [B, N, heads, D] (token raster
+    order over the T x H x W grid) -> o [B, N, heads, D]."""
+    T, H, W = grid
+    B, N, heads, D = q.shape
+    s = shape(B, heads, D, T, H, W)
+    q_t = tile_permute(q, s, LAYOUT_TOKEN_MAJOR)
+    k_t = tile_permute(k, s, LAYOUT_TOKEN_MAJOR)
+    v_t = tile_permute(v, s, LAYOUT_FEATURE_MAJOR)
+    row_ptr, col_idx, _ = build_mask(radii, scores, s, dense_count, r_max, with_routed=True)
+    o_t, _ = attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, s, scale, kv_chunk, with_lse=False)
+    return tile_unpermute(o_t, s)

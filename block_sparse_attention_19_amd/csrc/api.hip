@@ -1,0 +1,255 @@
+// C ABI of libvsa: argument validation on the host, then kernel launches.
+// Every check runs before anything is enqueued, so a call that returns an
+// error leaves the stream untouched.
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+
+#include "vsa_common.h"
+
+namespace vsa {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_cus[kMaxDevices] = {0};
+
+// CU count of the current device (LDS limits raised once per device).
+vsa_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("hipGetDevice failed: %s", hipGetErrorString(e));
+    return VSA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0) {
+      set_error("hipDeviceGetAttribute(CU count) failed: %s", hipGetErrorString(e));
+      return VSA_ERR_HIP;
+    }
+    e = attn_set_lds_limits();
+    if (e != hipSuccess) {
+      set_error("hipFuncSetAttribute(LDS) failed: %s", hipGetErrorString(e));
+      return VSA_ERR_HIP;
+    }
+    g_cus[dev] = n;
+  }
+  *cus = g_cus[dev];
+  return VSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+vsa_status check_shape(const vsa_shape* s) {
+  if (!s) { set_error("shape is NULL"); return VSA_ERR_INVALID_ARG; }
+  if (s->batch < 1 || s->heads < 1 || s->T < 1 || s->H < 1 || s->W < 1 || s->head_dim < 1) {
+    set_error("shape fields must be >= 1 (batch=%d heads=%d D=%d T=%d H=%d W=%d)", s->batch,
+              s->heads, s->head_dim, s->T, s->H, s->W);
+    return VSA_ERR_INVALID_ARG;
+  }
+  if (s->head_dim != 64 && s->head_dim != 128) {
+    set_error("head_dim %d not supported (64 or 128)", s->head_dim);
+    return VSA_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)s->batch * s->heads > 65535) {
+    set_error("batch * heads must be <= 65535");
+    return VSA_ERR_INVALID_ARG;
+  }
+  const Grid g = make_grid(*s);
+  const int64_t nT = (int64_t)((s->T + 3) / 4) * ((s->H + 3) / 4) * ((s->W + 3) / 4);
+  (void)g;
+  const int64_t rows = (int64_t)s->batch * s->heads * nT;
+  // rows and padded token rows are int32 in the CSR and the unit list.
+  if (nT * kTileTokens > INT_MAX || rows * kTileTokens > INT_MAX) {
+    set_error("problem too large: %lld tile rows", (long long)rows);
+    return VSA_ERR_OVERFLOW;
+  }
+  return VSA_OK;
+}
+
+vsa_status check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) { set_error("%s is NULL", name); return VSA_ERR_INVALID_ARG; }
+  if (!aligned(p, align)) {
+    set_error("%s is not %zu-byte aligned", name, align);
+    return VSA_ERR_INVALID_ARG;
+  }
+  return VSA_OK;
+}
+
+vsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return VSA_OK;
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return VSA_ERR_HIP;
+}
+
+int64_t window_bound(int64_t r, const Grid& g) {
+  // Unclipped window size of radius r, capped by the tile count.
+  int64_t total = 0;
+  for (int64_t dt = -r; dt <= r; ++dt) {
+    const int64_t s = r - (dt < 0 ? -dt : dt);
+    const int64_t side_h = std::min<int64_t>(2 * s + 1, g.nh);
+    const int64_t side_w = std::min<int64_t>(2 * s + 1, g.nw);
+    if (dt >= g.nt || -dt >= g.nt) continue;
+    total += side_h * side_w;
+  }
+  return std::min<int64_t>(total, g.nT);
+}
+
+#define VSA_TRY(x)                       \
+  do {                                   \
+    vsa_status _st = (x);                \
+    if (_st != VSA_OK) return _st;       \
+  } while (0)
+
+}  // namespace
+}  // namespace vsa
+
+using namespace vsa;
+
+extern "C" {
+
+const char* vsa_status_string(vsa_status s) {
+  switch (s) {
+    case VSA_OK: return "ok";
+    case VSA_ERR_INVALID_ARG: return "invalid argument";
+    case VSA_ERR_UNSUPPORTED: return "unsupported";
+    case VSA_ERR_CAPACITY: return "buffer too small";
+    case VSA_ERR_OVERFLOW: return "index overflow";
+    case VSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* vsa_last_error(void) { return g_err; }
+
+int32_t vsa_num_tiles(const vsa_shape* s) {
+  if (check_shape(s) != VSA_OK) return -1;
+  return make_grid(*s).nT;
+}
+
+vsa_status vsa_tile_permute(const vsa_shape* s, const void* x, void* x_tiled, int32_t layout,
+                            void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(x, 16, "x"));
+  VSA_TRY(check_ptr(x_tiled, 16, "x_tiled"));
+  if (layout != VSA_LAYOUT_TOKEN_MAJOR && layout != VSA_LAYOUT_FEATURE_MAJOR) {
+    set_error("unknown layout %d", layout);
+    return VSA_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_permute(*s, x, x_tiled, layout, static_cast<hipStream_t>(stream)),
+                    "tile permute launch");
+}
+
+vsa_status vsa_tile_unpermute(const vsa_shape* s, const void* o_tiled, void* o, void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(o_tiled, 16, "o_tiled"));
+  VSA_TRY(check_ptr(o, 16, "o"));
+  return hip_status(launch_unpermute(*s, o_tiled, o, static_cast<hipStream_t>(stream)),
+                    "tile unpermute launch");
+}
+
+int64_t vsa_mask_nnz_bound(const vsa_shape* s, int32_t r_max, int32_t dense_count) {
+  if (check_shape(s) != VSA_OK) return -1;
+  const Grid g = make_grid(*s);
+  if (r_max < 0 || r_max > 255 || dense_count < 0 || dense_count > g.nT) return -1;
+  const int64_t bh = (int64_t)s->batch * s->heads;
+  const int64_t local = window_bound(r_max, g);
+  return bh * ((int64_t)dense_count * g.nT + (int64_t)(g.nT - dense_count) * local);
+}
+
+size_t vsa_mask_workspace_bytes(const vsa_shape* s) {
+  if (check_shape(s) != VSA_OK) return 0;
+  return mask_workspace_bytes(*s);
+}
+
+vsa_status vsa_build_mask(const vsa_shape* s, const uint8_t* radii, const float* scores,
+                          int32_t dense_count, int32_t r_max, int32_t* row_ptr, int32_t* col_idx,
+                          int64_t col_capacity, uint8_t* routed, void* ws, size_t ws_bytes,
+                          void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(radii, 1, "radii"));
+  VSA_TRY(check_ptr(scores, 4, "scores"));
+  VSA_TRY(check_ptr(row_ptr, 4, "row_ptr"));
+  VSA_TRY(check_ptr(col_idx, 4, "col_idx"));
+  const Grid g = make_grid(*s);
+  if (dense_count < 0 || dense_count > g.nT) {
+    set_error("dense_count %d outside [0, %d]", dense_count, g.nT);
+    return VSA_ERR_INVALID_ARG;
+  }
+  if (r_max < 0 || r_max > 255) {
+    set_error("r_max %d outside [0, 255]", r_max);
+    return VSA_ERR_INVALID_ARG;
+  }
+  const int64_t bound = vsa_mask_nnz_bound(s, r_max, dense_count);
+  if (bound > INT_MAX) {
+    set_error("nnz bound %lld exceeds int32", (long long)bound);
+    return VSA_ERR_OVERFLOW;
+  }
+  if (col_capacity < bound) {
+    set_error("col_capacity %lld < nnz bound %lld", (long long)col_capacity, (long long)bound);
+    return VSA_ERR_CAPACITY;
+  }
+  if (!routed) {
+    VSA_TRY(check_ptr(ws, 16, "ws"));
+    if (ws_bytes < mask_workspace_bytes(*s)) {
+      set_error("mask workspace %zu < %zu bytes", ws_bytes, mask_workspace_bytes(*s));
+      return VSA_ERR_CAPACITY;
+    }
+  }
+  return hip_status(launch_build_mask(*s, radii, scores, dense_count, r_max, row_ptr, col_idx,
+                                      routed, ws, static_cast<hipStream_t>(stream)),
+                    "mask launch");
+}
+
+size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk) {
+  if (check_shape(s) != VSA_OK || kv_chunk < 0) return 0;
+  return attn_layout(*s, kv_chunk).total;
+}
+
+vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t, const void* v_t,
+                        const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o_t,
+                        float* lse_t, int32_t kv_chunk, void* ws, size_t ws_bytes, void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(q_t, 16, "q_t"));
+  VSA_TRY(check_ptr(k_t, 16, "k_t"));
+  VSA_TRY(check_ptr(v_t, 16, "v_t"));
+  VSA_TRY(check_ptr(row_ptr, 4, "row_ptr"));
+  VSA_TRY(check_ptr(col_idx, 4, "col_idx"));
+  VSA_TRY(check_ptr(o_t, 16, "o_t"));
+  if (lse_t) VSA_TRY(check_ptr(lse_t, 4, "lse_t"));
+  VSA_TRY(check_ptr(ws, 256, "ws"));
+  if (!(scale > 0.f) || scale > 3.0e38f) {
+    set_error("scale must be finite and > 0");
+    return VSA_ERR_INVALID_ARG;
+  }
+  if (kv_chunk < 0) {
+    set_error("kv_chunk must be >= 0");
+    return VSA_ERR_INVALID_ARG;
+  }
+  const size_t need = attn_layout(*s, kv_chunk).total;
+  if (ws_bytes < need) {
+    set_error("attention workspace %zu < %zu bytes", ws_bytes, need);
+    return VSA_ERR_CAPACITY;
+  }
+  int cus = 0;
+  VSA_TRY(device_cus(&cus));
+  return hip_status(launch_attn(*s, q_t, k_t, v_t, row_ptr, col_idx, scale, o_t, lse_t, kv_chunk,
+                                ws, cus, static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,696 @@
+// Block-sparse attention forward over tile-major Q/K/V, driven by a CSR of kept
+// key tiles per query tile.
+//
+// The pages ("Token Radius Attention for Efficient Video Generation", step 3;
+// "Triage: Skip, Skim, or Refine Attention Tiles in Video Diffusion
+// Transformers", fused kernel) execute attention only on the retained tiles of
+// a block-sparse mask.  The result is exactly masked softmax attention: every
+// key tile a query tile does not list contributes nothing, so the kernel walks
+// the listed tiles only.
+//
+// Execution model (CDNA4 / gfx950):
+//   * A workgroup is 4 waves (256 threads).  Each wave owns 32 query rows and
+//     keeps them in registers as the B operand of v_mfma_f32_32x32x16_bf16.
+//   * Scores are computed transposed, S^T = K Q^T, so that every lane ends up
+//     holding one query's scores: the row max / row sum are in-lane except for
+//     one exchange between the two 32-lane halves, and the probabilities P^T
+//     are already the B operand of the second product O^T = V^T P^T, whose
+//     accumulator again holds one query per lane (one rescale factor per lane).
+//   * K is staged in LDS as [64 keys][D], V as [D][64 keys] (the permute writes
+//     V feature-major), both XOR-swizzled so the 16-byte operand reads of a
+//     wave are bank-conflict free.  The 64 keys of a tile are read in an order
+//     (bits 2 and 3 of the row index swapped) that makes each lane's 8 P values
+//     one contiguous 16-byte V^T read.
+//   * Online softmax in fp32, base 2 (scale * log2 e folded into one FMA), with
+//     lazy rescaling: the running max only moves when a new score exceeds it
+//     by more than 2^8, which keeps P <= 256 and skips most O rescales.
+//   * Work units come from a device-side plan: "G" units pair two query tiles
+//     of one (batch, head) whose key lists are both complete (every key tile;
+//     routed rows) so one staged K/V tile feeds 4 waves; "S" units take one
+//     query tile and split its key list over two wave pairs, merged in LDS at
+//     the end.  Long G units are split into key chunks that write fp32
+//     partials (O, running max, sum) merged exactly by a combine kernel.
+//     Units are taken from an atomic counter by a persistent grid (2
+//     workgroups per CU), longest class first.
+#include "vsa_common.h"
+
+#include <limits.h>
+
+namespace vsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kPlanThreads = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
+constexpr int kMinChunk = 32;          // smallest automatic key chunk (tiles)
+// Automatic splitting aims at this many G units (4x the resident workgroups of
+// a 256-CU part at 2 workgroups per CU); fixed so workspace sizes do not depend
+// on the device.
+constexpr int kSplitTarget = 1024;
+
+struct Unit {
+  int32_t row[2];  // CSR rows (global); S units use row[0] only
+  int32_t kb, ke;  // key range [kb, ke): offsets into row[0]'s column list
+  int32_t slot;    // first partial slot, or -1: write the final output
+  int32_t mode;    // 0 = G (two query tiles share the keys), 1 = S (one tile, keys split)
+  int32_t pad[2];
+};
+static_assert(sizeof(Unit) == 32, "unit layout");
+
+struct Comb {
+  int32_t row, slot0, stride, n;
+};
+
+struct Header {
+  int32_t n_units;
+  int32_t counter;
+  int32_t n_comb;
+  int32_t chunks_g;
+  int32_t overflow;
+  int32_t pad[59];
+};
+static_assert(sizeof(Header) == 256, "header layout");
+
+}  // namespace
+
+// ------------------------------------------------------------ workspace
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+AttnLayout attn_layout(const vsa_shape& s, int kv_chunk) {
+  const Grid g = make_grid(s);
+  AttnLayout L;
+  L.bh = (int64_t)s.batch * s.heads;
+  L.rows = L.bh * g.nT;
+  const int64_t target = kSplitTarget;
+  if (kv_chunk > 0) {
+    const int64_t ch = (g.nT + kv_chunk - 1) / kv_chunk;
+    L.max_units = (L.rows / 2 + L.rows) * ch + 1;
+    L.max_slots = L.rows * ch;
+  } else {
+    L.max_units = L.rows / 2 + 2 * target + L.rows + 1;
+    L.max_slots = 4 * target;
+  }
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+  take(sizeof(Header));
+  L.off_E = take(4 * (L.rows + 1));
+  L.off_gbase = take(4 * (L.bh + 1));
+  L.off_grows = take(4 * (L.rows + 2));
+  L.off_sinfo = take(4 * (L.rows + 1));
+  L.off_su = take(4 * (L.rows + 1));
+  L.off_sp = take(4 * (L.rows + 1));
+  L.off_sc = take(4 * (L.rows + 1));
+  L.off_units = take(sizeof(Unit) * L.max_units);
+  L.off_comb = take(sizeof(Comb) * (L.rows + 1));
+  L.off_po = take((size_t)L.max_slots * kTileTokens * s.head_dim * 4);
+  L.off_pml = take((size_t)L.max_slots * kTileTokens * 2 * 4);
+  L.total = o;
+  return L;
+}
+
+namespace {
+
+// ------------------------------------------------------------------ plan
+
+struct PlanArgs {
+  const int* row_ptr;
+  int bh, nT, kv_chunk, target;
+  int64_t max_units, max_slots;
+  Header* hdr;
+  int *E, *gbase, *grows, *sinfo, *su, *sp, *sc;
+  Unit* units;
+  Comb* comb;
+};
+
+// Exclusive scan of one int per thread over the 1024-thread block; returns the
+// thread's prefix and writes the total to *total.
+__device__ int block_exclusive_scan(int v, int* buf, int* total) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int add = (threadIdx.x >= off) ? buf[threadIdx.x - off] : 0;
+    __syncthreads();
+    buf[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const int incl = buf[threadIdx.x];
+  *total = buf[kPlanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
+  __shared__ int buf[kPlanThreads];
+  __shared__ int s_chunk_g, s_sg;
+  const int nT = p.nT;
+  const int64_t rows = (int64_t)p.bh * nT;
+  const int64_t seg = (rows + kPlanThreads - 1) / kPlanThreads;
+  const int64_t r0 = min(rows, seg * threadIdx.x), r1 = min(rows, r0 + seg);
+  auto len_of = [&](int64_t r) { return p.row_ptr[r + 1] - p.row_ptr[r]; };
+
+  // A: E[r] = number of complete rows (every key tile) before row r.
+  int cnt = 0;
+  for (int64_t r = r0; r < r1; ++r) cnt += (len_of(r) == nT);
+  int tot;
+  int base = block_exclusive_scan(cnt, buf, &tot);
+  for (int64_t r = r0; r < r1; ++r) {
+    p.E[r] = base;
+    base += (len_of(r) == nT);
+  }
+  if (threadIdx.x == 0) p.E[rows] = tot;
+  __syncthreads();
+
+  // A2: pairs of complete rows per (b, h) -> G groups; gbase = exclusive scan.
+  const int64_t segb = (p.bh + kPlanThreads - 1) / kPlanThreads;
+  const int64_t b0 = min((int64_t)p.bh, segb * threadIdx.x), b1 = min((int64_t)p.bh, b0 + segb);
+  int gcnt = 0;
+  for (int64_t b = b0; b < b1; ++b) gcnt += (p.E[(b + 1) * nT] - p.E[b * nT]) / 2;
+  int NG;
+  int gb = block_exclusive_scan(gcnt, buf, &NG);
+  for (int64_t b = b0; b < b1; ++b) {
+    p.gbase[b] = gb;
+    gb += (p.E[(b + 1) * nT] - p.E[b * nT]) / 2;
+  }
+  if (threadIdx.x == 0) {
+    p.gbase[p.bh] = NG;
+    int chunk;
+    if (p.kv_chunk > 0) {
+      chunk = p.kv_chunk;
+    } else {
+      int s = 1;
+      if (NG > 0) s = max(1, (p.target + NG - 1) / NG);
+      s = min(s, max(1, nT / kMinChunk));
+      chunk = (nT + s - 1) / s;
+    }
+    chunk = max(1, min(chunk, max(nT, 1)));
+    s_chunk_g = chunk;
+    s_sg = (nT + chunk - 1) / chunk;
+  }
+  __syncthreads();
+  const int chunk_g = s_chunk_g, sg = (nT > 0) ? s_sg : 1;
+  const int chunk_s = (p.kv_chunk > 0) ? p.kv_chunk : INT_MAX;
+
+  // B: place G members, mark S rows with their chunk count.
+  for (int64_t r = r0; r < r1; ++r) {
+    const int len = len_of(r);
+    const int64_t b = r / nT;
+    const int e0 = p.E[b * nT];
+    const int fc = p.E[(b + 1) * nT] - e0;
+    int n = 0;
+    if (len == nT && nT > 0 && (p.E[r] - e0) < (fc / 2) * 2) {
+      const int j = p.E[r] - e0;
+      p.grows[(p.gbase[b] + j / 2) * 2 + (j & 1)] = (int)r;
+    } else {
+      n = (len <= 0) ? 1 : (int)((len + (int64_t)chunk_s - 1) / chunk_s);
+    }
+    p.sinfo[r] = n;
+  }
+  __syncthreads();
+
+  // C: scans of S units, S partial slots and S combine entries.
+  int c_su = 0, c_sp = 0, c_sc = 0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const int n = p.sinfo[r];
+    c_su += n;
+    c_sp += (n > 1) ? n : 0;
+    c_sc += (n > 1);
+  }
+  int nSU, nSP, nSC;
+  int bu = block_exclusive_scan(c_su, buf, &nSU);
+  int bp = block_exclusive_scan(c_sp, buf, &nSP);
+  int bc = block_exclusive_scan(c_sc, buf, &nSC);
+  for (int64_t r = r0; r < r1; ++r) {
+    const int n = p.sinfo[r];
+    p.su[r] = bu;
+    p.sp[r] = bp;
+    p.sc[r] = bc;
+    bu += n;
+    bp += (n > 1) ? n : 0;
+    bc += (n > 1);
+  }
+  __syncthreads();
+
+  const int64_t nGU = (int64_t)NG * sg;
+  const int64_t gslots = (sg > 1) ? 2 * nGU : 0;
+  const int64_t n_units = nGU + nSU;
+  const int64_t n_comb = ((sg > 1) ? 2LL * NG : 0) + nSC;
+  if (n_units > p.max_units || gslots + nSP > p.max_slots) {
+    if (threadIdx.x == 0) {
+      p.hdr->n_units = 0;
+      p.hdr->n_comb = 0;
+      p.hdr->overflow = 1;
+      p.hdr->counter = 0;
+    }
+    return;
+  }
+
+  // D: emit units (G first: the longest) and combine entries.
+  for (int64_t i = threadIdx.x; i < nGU; i += kPlanThreads) {
+    const int gi = (int)(i / sg), c = (int)(i % sg);
+    Unit u;
+    u.row[0] = p.grows[2 * gi];
+    u.row[1] = p.grows[2 * gi + 1];
+    u.kb = c * chunk_g;
+    u.ke = min(nT, u.kb + chunk_g);
+    u.slot = (sg > 1) ? (int)(2 * i) : -1;
+    u.mode = 0;
+    u.pad[0] = u.pad[1] = 0;
+    p.units[i] = u;
+  }
+  if (sg > 1) {
+    for (int64_t i = threadIdx.x; i < 2LL * NG; i += kPlanThreads) {
+      const int gi = (int)(i / 2), q = (int)(i & 1);
+      Comb cb;
+      cb.row = p.grows[2 * gi + q];
+      cb.slot0 = 2 * gi * sg + q;
+      cb.stride = 2;
+      cb.n = sg;
+      p.comb[i] = cb;
+    }
+  }
+  const int64_t comb_base = (sg > 1) ? 2LL * NG : 0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const int n = p.sinfo[r];
+    if (n == 0) continue;
+    const int len = len_of(r);
+    const int ch = (n > 1) ? chunk_s : max(len, 0);
+    for (int c = 0; c < n; ++c) {
+      Unit u;
+      u.row[0] = (int)r;
+      u.row[1] = -1;
+      u.kb = c * ch;
+      u.ke = min(len, u.kb + ch);
+      if (u.ke < u.kb) u.ke = u.kb;
+      u.slot = (n > 1) ? (int)(gslots + p.sp[r] + c) : -1;
+      u.mode = 1;
+      u.pad[0] = u.pad[1] = 0;
+      p.units[nGU + p.su[r] + c] = u;
+    }
+    if (n > 1) {
+      Comb cb;
+      cb.row = (int)r;
+      cb.slot0 = (int)(gslots + p.sp[r]);
+      cb.stride = 1;
+      cb.n = n;
+      p.comb[comb_base + p.sc[r]] = cb;
+    }
+  }
+  if (threadIdx.x == 0) {
+    p.hdr->n_units = (int)n_units;
+    p.hdr->n_comb = (int)n_comb;
+    p.hdr->chunks_g = sg;
+    p.hdr->overflow = 0;
+    p.hdr->counter = 0;
+  }
+}
+
+// -------------------------------------------------------------- attention
+
+struct AttnArgs {
+  const uint16_t* q;   // [BH][nT*64][D]
+  const uint16_t* k;   // [BH][nT*64][D]
+  const uint16_t* v;   // [BH][nT][D][64]
+  const int* row_ptr;
+  const int* col_idx;
+  uint16_t* o;         // [BH][nT*64][D]
+  float* lse;          // [BH][nT*64] or null
+  const Header* hdr;
+  Header* hdr_mut;
+  const Unit* units;
+  float* part_o;       // [slots][64][D]
+  float* part_ml;      // [slots][2][64]
+  int nT, nh, nw, T, H, W;
+  float c2;            // scale * log2(e)
+};
+
+// Row index of the K operand for A-operand row rho: bits 2 and 3 swapped.
+__device__ __forceinline__ int sigma(int rho) {
+  return (rho & 0x13) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+
+template <int D>
+struct Cfg {
+  static constexpr int kRowBytes = D * 2;             // K row in LDS
+  static constexpr int kChunks = D / 8;               // 16-byte chunks per K row
+  static constexpr int kTileBytes = kTileTokens * D * 2;
+  static constexpr int kSlotBytes = 2 * kTileBytes;   // K + V^T
+  static constexpr int kKSteps = D / 16;              // k-steps of Q.K^T
+  static constexpr int kDBlocks = D / 32;             // 32-row blocks of O^T
+};
+
+// LDS byte offset of 16-byte chunk c of K row `row` (swizzled).
+template <int D>
+__device__ __forceinline__ int k_off(int row, int c) {
+  const int sw = (D == 128) ? (row & 15) : ((row >> 1) & 7);
+  return row * Cfg<D>::kRowBytes + ((c ^ sw) << 4);
+}
+// LDS byte offset of 16-byte chunk c (8 keys) of V^T row d (swizzled).
+__device__ __forceinline__ int v_off(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
+
+// Copy one K tile and one V^T tile into an LDS slot, `nthr` threads starting
+// at thread index `t0` of the workgroup.
+template <int D>
+__device__ __forceinline__ void stage_tile(char* slot, const uint4* kt, const uint4* vt, int tid,
+                                           int nthr) {
+  constexpr int kChunksPerTile = Cfg<D>::kTileBytes / 16;
+  for (int i = tid; i < kChunksPerTile; i += nthr) {
+    const uint4 kv = kt[i];
+    const uint4 vv = vt[i];
+    const int kr = i / Cfg<D>::kChunks, kc = i % Cfg<D>::kChunks;
+    *reinterpret_cast<uint4*>(slot + k_off<D>(kr, kc)) = kv;
+    const int vr = i >> 3, vc = i & 7;
+    *reinterpret_cast<uint4*>(slot + Cfg<D>::kTileBytes + v_off(vr, vc)) = vv;
+  }
+}
+
+template <int D>
+struct WaveState {
+  bf16x8 qreg[Cfg<D>::kKSteps];
+  f32x16 o[Cfg<D>::kDBlocks];
+  float m;  // running max (log2 domain, scaled)
+  float l;  // this lane's partial sum of P
+};
+
+template <int D>
+__device__ __forceinline__ void process_tile(WaveState<D>& st, const char* slot, int lane,
+                                             uint64_t vmask, float c2) {
+  const int q = lane & 31, h = lane >> 5;
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  const int krow0 = sigma(q);
+#pragma unroll
+  for (int t = 0; t < Cfg<D>::kKSteps; ++t) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + k_off<D>(32 * kb + krow0, 2 * t + h));
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[t], s[kb], 0, 0, 0);
+    }
+  }
+  // key index of register r of block kb in this lane: 32kb + 16(r/8) + 8h + r%8
+  if (vmask != ~0ull) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
+        if (!((vmask >> key) & 1ull)) s[kb][r] = -INFINITY;
+      }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mc = mx * c2;
+  if (__any(mc > st.m + kRescaleSlack)) {
+    const float mn = fmaxf(st.m, mc);
+    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+    st.m = mn;
+  }
+  const float mneg = (st.m == -INFINITY) ? 0.f : -st.m;
+  bf16x8 pb[2][2];
+  float lsum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, mneg));
+      lsum += pv;
+      pb[kb][r >> 3][r & 7] = (__bf16)pv;
+    }
+  st.l += lsum;
+#pragma unroll
+  for (int db = 0; db < Cfg<D>::kDBlocks; ++db) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            slot + Cfg<D>::kTileBytes + v_off(32 * db + q, 4 * kb + 2 * s2 + h));
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][s2], st.o[db], 0, 0, 0);
+      }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_unit;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = lane & 31, h = lane >> 5;
+  const int nT = args.nT;
+  const int n_units = args.hdr->n_units;
+  const float c2 = args.c2;
+
+  for (;;) {
+    if (tid == 0) s_unit = atomicAdd(&args.hdr_mut->counter, 1);
+    __syncthreads();
+    const int ui = s_unit;
+    __syncthreads();
+    if (ui >= n_units) break;
+    const Unit u = args.units[ui];
+    const bool g_mode = (u.mode == 0);
+    const int half = wave & 1;
+    const int grp = wave >> 1;            // G: which query tile; S: which key split
+    const int row = g_mode ? u.row[grp] : u.row[0];
+    const int64_t bh = row / nT;
+    const int64_t qrow0 = (int64_t)row * kTileTokens + 32 * half;  // == (bh*nT + a)*64 + 32*half
+
+    WaveState<D> st;
+    {
+      const uint16_t* qp = args.q + (qrow0 + q) * D + 8 * h;
+#pragma unroll
+      for (int t = 0; t < Cfg<D>::kKSteps; ++t)
+        st.qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
+    }
+#pragma unroll
+    for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
+    st.m = -INFINITY;
+    st.l = 0.f;
+
+    const int cbase = args.row_ptr[u.row[0]];
+    const int nkeys = u.ke - u.kb;
+    const int nsteps = g_mode ? nkeys : (nkeys + 1) / 2;
+    const uint4* kbase = reinterpret_cast<const uint4*>(args.k + bh * (int64_t)nT * kTileTokens * D);
+    const uint4* vbase = reinterpret_cast<const uint4*>(args.v + bh * (int64_t)nT * kTileTokens * D);
+    constexpr int kTileChunks = Cfg<D>::kTileBytes / 16;
+
+    for (int step = 0; step < nsteps; ++step) {
+      // stage this step's tile(s)
+      int my_tile = -1;
+      if (g_mode) {
+        const int j = args.col_idx[cbase + u.kb + step];
+        stage_tile<D>(smem, kbase + (int64_t)j * kTileChunks, vbase + (int64_t)j * kTileChunks, tid,
+                      kThreads);
+        my_tile = j;
+      } else {
+        const int pos = u.kb + 2 * step + grp;
+        if (pos < u.ke) {
+          const int j = args.col_idx[cbase + pos];
+          stage_tile<D>(smem + grp * Cfg<D>::kSlotBytes, kbase + (int64_t)j * kTileChunks,
+                        vbase + (int64_t)j * kTileChunks, tid & 127, 128);
+          my_tile = j;
+        }
+      }
+      __syncthreads();
+      if (my_tile >= 0) {
+        const uint64_t vm = tile_valid_mask(my_tile, args.nh, args.nw, args.T, args.H, args.W);
+        process_tile<D>(st, smem + (g_mode ? 0 : grp * Cfg<D>::kSlotBytes), lane, vm, c2);
+      }
+      __syncthreads();
+    }
+
+    // S units: merge the two key splits (waves 2,3 -> waves 0,1) through LDS.
+    if (!g_mode) {
+      float* xo = reinterpret_cast<float*>(smem) + half * (64 * (Cfg<D>::kDBlocks * 16 + 2));
+      if (grp == 1) {
+#pragma unroll
+        for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = st.o[db][r];
+        xo[Cfg<D>::kDBlocks * 16 * 64 + lane] = st.m;
+        xo[(Cfg<D>::kDBlocks * 16 + 1) * 64 + lane] = st.l;
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const float m1 = xo[Cfg<D>::kDBlocks * 16 * 64 + lane];
+        const float l1 = xo[(Cfg<D>::kDBlocks * 16 + 1) * 64 + lane];
+        const float mm = fmaxf(st.m, m1);
+        const float w0 = (mm == -INFINITY) ? 0.f : exp2f(st.m - mm);
+        const float w1 = (mm == -INFINITY) ? 0.f : exp2f(m1 - mm);
+#pragma unroll
+        for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st.o[db][r] = w0 * st.o[db][r] + w1 * xo[(db * 16 + r) * 64 + lane];
+        st.l = w0 * st.l + w1 * l1;
+        st.m = mm;
+      }
+      __syncthreads();
+    }
+
+    const bool writer = g_mode || grp == 0;
+    if (writer) {
+      const float lt = st.l + __shfl_xor(st.l, 32);
+      const int qi = 32 * half + q;  // query row within the tile
+      if (u.slot < 0) {
+        const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+        uint16_t* op = args.o + (qrow0 + q) * D + 4 * h;
+#pragma unroll
+        for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            __bf16 b0 = (__bf16)(st.o[db][4 * g + 0] * inv);
+            __bf16 b1 = (__bf16)(st.o[db][4 * g + 1] * inv);
+            __bf16 b2 = (__bf16)(st.o[db][4 * g + 2] * inv);
+            __bf16 b3 = (__bf16)(st.o[db][4 * g + 3] * inv);
+            uint2 w;
+            w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+            w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+            *reinterpret_cast<uint2*>(op + 32 * db + 8 * g) = w;
+          }
+        if (args.lse && h == 0)
+          args.lse[qrow0 + q] = (lt > 0.f) ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t slot = u.slot + (g_mode ? grp : 0);
+        float* po = args.part_o + slot * kTileTokens * D + (int64_t)qi * D + 4 * h;
+#pragma unroll
+        for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(po + 32 * db + 8 * g) =
+                make_float4(st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2], st.o[db][4 * g + 3]);
+        if (h == 0) {
+          args.part_ml[slot * 128 + qi] = st.m;
+          args.part_ml[slot * 128 + 64 + qi] = lt;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const Header* hdr, const Comb* comb,
+                                                      const float* part_o, const float* part_ml,
+                                                      uint16_t* o, float* lse) {
+  const int n_comb = hdr->n_comb;
+  constexpr int kVec = D / 4;                    // float4 per row
+  for (int ci = blockIdx.x; ci < n_comb; ci += gridDim.x) {
+    const Comb c = comb[ci];
+    const int64_t orow0 = (int64_t)c.row * kTileTokens;
+    for (int i = threadIdx.x; i < kTileTokens * kVec; i += blockDim.x) {
+      const int r = i / kVec, v4 = i % kVec;
+      float M = -INFINITY;
+      for (int s = 0; s < c.n; ++s) M = fmaxf(M, part_ml[(int64_t)(c.slot0 + s * c.stride) * 128 + r]);
+      float L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < c.n; ++s) {
+        const int64_t slot = c.slot0 + (int64_t)s * c.stride;
+        const float m = part_ml[slot * 128 + r];
+        const float w = (M == -INFINITY) ? 0.f : exp2f(m - M);
+        L += w * part_ml[slot * 128 + 64 + r];
+        const float4 x = *reinterpret_cast<const float4*>(part_o + (slot * kTileTokens + r) * D + 4 * v4);
+        acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+      }
+      const float inv = (L > 0.f) ? 1.f / L : 0.f;
+      __bf16 b0 = (__bf16)(acc.x * inv), b1 = (__bf16)(acc.y * inv);
+      __bf16 b2 = (__bf16)(acc.z * inv), b3 = (__bf16)(acc.w * inv);
+      uint2 w2;
+      w2.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      w2.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+      *reinterpret_cast<uint2*>(o + (orow0 + r) * D + 4 * v4) = w2;
+      if (lse && v4 == 0) lse[orow0 + r] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const void* v,
+                       const int* row_ptr, const int* col_idx, float scale, void* o, float* lse,
+                       int kv_chunk, void* ws, int cus, hipStream_t stream) {
+  const Grid g = make_grid(s);
+  const AttnLayout L = attn_layout(s, kv_chunk);
+  char* w = static_cast<char*>(ws);
+  Header* hdr = reinterpret_cast<Header*>(w);
+  PlanArgs pa;
+  pa.row_ptr = row_ptr;
+  pa.bh = (int)L.bh;
+  pa.nT = g.nT;
+  pa.kv_chunk = kv_chunk;
+  pa.target = kSplitTarget;
+  pa.max_units = L.max_units;
+  pa.max_slots = L.max_slots;
+  pa.hdr = hdr;
+  pa.E = reinterpret_cast<int*>(w + L.off_E);
+  pa.gbase = reinterpret_cast<int*>(w + L.off_gbase);
+  pa.grows = reinterpret_cast<int*>(w + L.off_grows);
+  pa.sinfo = reinterpret_cast<int*>(w + L.off_sinfo);
+  pa.su = reinterpret_cast<int*>(w + L.off_su);
+  pa.sp = reinterpret_cast<int*>(w + L.off_sp);
+  pa.sc = reinterpret_cast<int*>(w + L.off_sc);
+  pa.units = reinterpret_cast<Unit*>(w + L.off_units);
+  pa.comb = reinterpret_cast<Comb*>(w + L.off_comb);
+  plan_kernel<<<1, kPlanThreads, 0, stream>>>(pa);
+
+  AttnArgs aa;
+  aa.q = static_cast<const uint16_t*>(q);
+  aa.k = static_cast<const uint16_t*>(k);
+  aa.v = static_cast<const uint16_t*>(v);
+  aa.row_ptr = row_ptr;
+  aa.col_idx = col_idx;
+  aa.o = static_cast<uint16_t*>(o);
+  aa.lse = lse;
+  aa.hdr = hdr;
+  aa.hdr_mut = hdr;
+  aa.units = pa.units;
+  aa.part_o = reinterpret_cast<float*>(w + L.off_po);
+  aa.part_ml = reinterpret_cast<float*>(w + L.off_pml);
+  aa.nT = g.nT;
+  aa.nh = g.nh;
+  aa.nw = g.nw;
+  aa.T = s.T;
+  aa.H = s.H;
+  aa.W = s.W;
+  aa.c2 = scale * kLog2e;
+  const int grid = (int)std::min<int64_t>(L.max_units, 2LL * cus);
+  if (s.head_dim == 128) {
+    const size_t lds = 2 * Cfg<128>::kSlotBytes;
+    attn_kernel<128><<<grid, kThreads, lds, stream>>>(aa);
+    combine_kernel<128><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
+  } else {
+    const size_t lds = 2 * Cfg<64>::kSlotBytes;
+    attn_kernel<64><<<grid, kThreads, lds, stream>>>(aa);
+    combine_kernel<64><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
+  }
+  return hipGetLastError();
+}
+
+hipError_t attn_set_lds_limits() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<128>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Cfg<128>::kSlotBytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<64>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Cfg<64>::kSlotBytes);
+}
+
+}  // namespace vsa

@@ -1,0 +1,180 @@
+/*
+ * vsa.h -- block-sparse self-attention over a video DiT's spatio-temporal token
+ * grid, for AMD Instinct MI355X (gfx950).  C ABI of libvsa.so.
+ *
+ * What the library computes
+ * -------------------------
+ * Tokens of a T x H x W latent grid are grouped into 4x4x4 tiles and stored
+ * tile-major ("Token Radius Attention for Efficient Video Generation", TRA,
+ * pipeline step 3: a tile-major token layout so that sparse supports become
+ * whole blocks).  Query tile a keeps key tile b when b lies in a local window
+ * whose radius r_a shrinks with temporal distance (TRA step 2: a per-query
+ * base radius applied across frames with a temporal distance-decay rule); the
+ * rule used here, in tile units, is
+ *     |dt| <= r_a  and  max(|dh|, |dw|) <= r_a - |dt|,
+ * with (dt, dh, dw) the tile-coordinate offset b - a.  A routed subset of the
+ * query tiles -- the `dense_count` tiles with the highest routing score per
+ * (batch, head) -- attends to every key tile instead ("Where Compute Matters:
+ * Heterogeneous Attention for Efficient Video Diffusion", abstract: uncertain
+ * tokens take dense global attention, the rest local attention, about 20%
+ * dense).  Attention is softmax(scale * q.k) v over the kept keys.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tile grid: nTt = ceil(T/4), nTh = ceil(H/4), nTw = ceil(W/4),
+ *   nT = nTt*nTh*nTw; tile index tau = (tt*nTh + th)*nTw + tw; slot of a token
+ *   inside its tile = (lt*4 + lh)*4 + lw.  Raster token index
+ *   n = (t*H + h)*W + w.  N = T*H*W, Npad = 64*nT.
+ * - bf16 is bfloat16 stored as 16-bit words.  All device pointers must be
+ *   16-byte aligned and point to device memory allocated by the caller; the
+ *   library never allocates, frees, synchronises or keeps a pointer after the
+ *   call returns.  Work is enqueued asynchronously on `stream` (a hipStream_t
+ *   passed as void*, NULL = the null stream); inputs are only read.
+ * - Arguments are checked on the host before anything is enqueued; a call that
+ *   returns an error has enqueued nothing.  Faults inside kernels surface at
+ *   the caller's next synchronisation of the stream.
+ * - Results are deterministic: bitwise identical across runs for the same
+ *   arguments.
+ */
+#ifndef VSA_H_
+#define VSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vsa_status {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or count   */
+  VSA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement    */
+  VSA_ERR_CAPACITY = 3,    /* an output or workspace buffer is too small     */
+  VSA_ERR_OVERFLOW = 4,    /* an index would not fit the int32 layouts       */
+  VSA_ERR_HIP = 5          /* the HIP runtime refused a launch               */
+} vsa_status;
+
+/* Problem shape.  head_dim must be 64 or 128; batch, heads, T, H, W >= 1. */
+typedef struct vsa_shape {
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t T, H, W;
+} vsa_shape;
+
+/* Layouts of a tile-major tensor (argument `layout` of vsa_tile_permute). */
+enum {
+  /* [B][heads][nT*64][D]: token rows of tile tau at rows tau*64 .. tau*64+63. */
+  VSA_LAYOUT_TOKEN_MAJOR = 0,
+  /* [B][heads][nT][D][64]: per tile, feature-major (the 64 slots of a tile
+   * are contiguous for each feature).  This is the layout vsa_attn_fwd takes
+   * for V. */
+  VSA_LAYOUT_FEATURE_MAJOR = 1
+};
+
+/* Human-readable name of a status code (static string). */
+const char* vsa_status_string(vsa_status s);
+
+/* Number of tiles nT of a shape, or -1 if the shape is invalid. */
+int32_t vsa_num_tiles(const vsa_shape* s);
+
+/* Last error text of the calling thread (static storage, never NULL). */
+const char* vsa_last_error(void);
+
+/* ---------------------------------------------------------------- permute
+ * vsa_tile_permute: gather raster tokens into the tile-major layout (TRA,
+ * pipeline step 3).
+ *   x        bf16 [B][N][heads][D]  (the layout a DiT's QKV projection gives)
+ *   x_tiled  bf16, layout per `layout` (see above); every element is written;
+ *            slots of padding tokens (outside the T x H x W grid) get +0.0.
+ * Errors: INVALID_ARG for a bad shape / pointer / layout; OVERFLOW if an
+ * element count exceeds 2^31 per (batch, head) plane.
+ */
+vsa_status vsa_tile_permute(const vsa_shape* s, const void* x, void* x_tiled,
+                            int32_t layout, void* stream);
+
+/* vsa_tile_unpermute: inverse of the token-major permute for the attention
+ * output; padded rows of o_tiled are never read.
+ *   o_tiled  bf16 [B][heads][nT*64][D]
+ *   o        bf16 [B][N][heads][D]
+ */
+vsa_status vsa_tile_unpermute(const vsa_shape* s, const void* o_tiled, void* o,
+                              void* stream);
+
+/* ------------------------------------------------------------------- mask
+ * Upper bound of the number of kept (query tile, key tile) pairs when every
+ * radius is <= r_max and `dense_count` tiles per (batch, head) are routed.
+ * Returns -1 for an invalid shape or count.
+ */
+int64_t vsa_mask_nnz_bound(const vsa_shape* s, int32_t r_max, int32_t dense_count);
+
+/* Device workspace (bytes) that vsa_build_mask needs. */
+size_t vsa_mask_workspace_bytes(const vsa_shape* s);
+
+/* vsa_build_mask: per-tile radii and routing scores -> CSR list of kept key
+ * tiles per query tile (TRA step 3: radii translated into a block-sparse mask).
+ *   radii        uint8 [B][heads][nT], tile units.  A radius above r_max is
+ *                treated as r_max (so the output always fits the bound).
+ *   scores       float32 [B][heads][nT].  Per (b, h) the dense_count tiles
+ *                first in the order (score descending by IEEE-754 totalOrder,
+ *                i.e. +NaN > +inf > ... > +0 > -0 > ... > -NaN; then lower tile
+ *                index) are routed dense.
+ *   dense_count  0 <= dense_count <= nT.
+ *   r_max        0 <= r_max <= 255.
+ *   row_ptr      int32 [B*heads*nT + 1]: row (b, h, a) at index
+ *                (b*heads + h)*nT + a; row_ptr[0] = 0.
+ *   col_idx      int32 [col_capacity]: each row's key tiles, strictly
+ *                ascending, the query tile itself always present.
+ *   col_capacity must be >= vsa_mask_nnz_bound(s, r_max, dense_count).
+ *   routed       optional uint8 [B][heads][nT] (NULL to skip): 1 if routed.
+ *   ws, ws_bytes device workspace of at least vsa_mask_workspace_bytes(s).
+ * Errors: INVALID_ARG, CAPACITY (col_capacity or ws too small), OVERFLOW
+ * (the nnz bound exceeds INT32_MAX).
+ */
+vsa_status vsa_build_mask(const vsa_shape* s, const uint8_t* radii, const float* scores,
+                          int32_t dense_count, int32_t r_max, int32_t* row_ptr,
+                          int32_t* col_idx, int64_t col_capacity, uint8_t* routed,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* -------------------------------------------------------------- attention
+ * Device workspace (bytes) that vsa_attn_fwd needs for this shape and
+ * kv_chunk (0 = automatic splitting).
+ */
+size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk);
+
+/* vsa_attn_fwd: block-sparse attention forward over the tile-major layout.
+ * Walks only the key tiles listed in the CSR, with bf16 MFMA products, fp32
+ * online softmax and accumulation; long rows are split across workgroups
+ * and merged exactly by log-sum-exp (the split never changes which keys a
+ * query sees, only the fp32 summation order).
+ *   q_t      bf16 [B][heads][nT*64][D]  (VSA_LAYOUT_TOKEN_MAJOR)
+ *   k_t      bf16 [B][heads][nT*64][D]  (VSA_LAYOUT_TOKEN_MAJOR)
+ *   v_t      bf16 [B][heads][nT][D][64] (VSA_LAYOUT_FEATURE_MAJOR)
+ *   row_ptr, col_idx: a CSR as vsa_build_mask writes it (rows (b, h, a);
+ *            columns ascending, in [0, nT)); any such CSR is accepted.
+ *            A row with no column yields zeros and LSE = -inf.
+ *   scale    softmax scale (1/sqrt(D) for standard attention), finite, > 0.
+ *   o_t      bf16 [B][heads][nT*64][D]: outputs; rows of padding query slots
+ *            hold unspecified values.
+ *   lse_t    optional float32 [B][heads][nT*64] (NULL to skip): natural-log
+ *            sum of exp(scale*q.k) over the kept valid keys.
+ *   kv_chunk 0 = automatic; > 0 = split every row into chunks of at most
+ *            kv_chunk key tiles (for testing split invariance).
+ *   ws, ws_bytes device workspace of at least vsa_attn_workspace_bytes(s,
+ *            kv_chunk); its contents need no initialisation.
+ * Padding keys (slots outside the grid) are excluded from every softmax by
+ * position, whatever values they hold.
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim not 64/128), CAPACITY (ws),
+ * OVERFLOW.
+ */
+vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t,
+                        const void* v_t, const int32_t* row_ptr, const int32_t* col_idx,
+                        float scale, void* o_t, float* lse_t, int32_t kv_chunk,
+                        void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H_ */

@@ -1,0 +1,45 @@
+"""Helpers shared by the GPU tests (device transfer, error statistics)."""
+import sys
+
+import numpy as np
+import torch
+
+from oracle import vsa_oracle as vo
+
+MAX_ABS = 2e-2     # bf16-in / fp32-accumulate output tolerance (max |delta|)
+MEAN_REL = 3e-3    # sum |delta| / sum |ref| over compared outputs
+LSE_ABS = 2e-3     # fp32 log-sum-exp
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def bf16_to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f64_of(t: torch.Tensor) -> np.ndarray:
+    return vo.bf16_to_f64(bits_of(t))
+
+
+def err_stats(got: np.ndarray, ref: np.ndarray):
+    d = np.abs(got - ref)
+    return float(d.max()), float(d.sum() / max(np.abs(ref).sum(), 1e-300))
+
+
+def assert_close(got, ref, what=""):
+    mx, mr = err_stats(got, ref)
+    say(f"  {what}: max_abs={mx:.3e} mean_rel={mr:.3e} (n={ref.size})")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert mx <= MAX_ABS, f"{what}: max_abs {mx} > {MAX_ABS}"
+    assert mr <= MEAN_REL, f"{what}: mean_rel {mr} > {MEAN_REL}"

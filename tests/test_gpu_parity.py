@@ -1,0 +1,226 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bit-exact: tile permute / unpermute (both layouts) and the CSR mask.
+Tolerance (max-abs 2e-2, mean-rel 3e-3): attention outputs, full rows on small
+grids and sampled query tiles at the full workload sizes."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import LSE_ABS, assert_close, bf16_to_dev, bits_of, dev, f64_of, say
+from oracle import vsa_oracle as vo
+
+pytestmark = pytest.mark.gpu
+
+vsa = pytest.importorskip("block_sparse_attention_19_amd")
+
+if not torch.cuda.is_available():  # collected on CPU hosts only to be deselected
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _shape(w):
+    return vsa.shape(w.batch, w.heads, w.D, w.T, w.H, w.W)
+
+
+def _run_all(w, q, k, v, r, s, kcount, kv_chunk=0, r_max=None):
+    sh = _shape(w)
+    qd, kd, vd = bf16_to_dev(q), bf16_to_dev(k), bf16_to_dev(v)
+    q_t = vsa.tile_permute(qd, sh, vsa.LAYOUT_TOKEN_MAJOR)
+    k_t = vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR)
+    v_t = vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR)
+    rp, ci, routed = vsa.build_mask(torch.from_numpy(r).to(dev()), torch.from_numpy(s).to(dev()),
+                                    sh, kcount, r_max if r_max is not None else max(w.radius_set))
+    o_t, lse = vsa.attn_fwd(q_t, k_t, v_t, rp, ci, sh, w.scale, kv_chunk)
+    o = vsa.tile_unpermute(o_t, sh)
+    torch.cuda.synchronize()
+    return dict(q_t=q_t, k_t=k_t, v_t=v_t, rp=rp, ci=ci, routed=routed, o_t=o_t, lse=lse, o=o)
+
+
+# ------------------------------------------------------------------ permute
+
+PERMUTE_CASES = [(8, 16, 16, 2, 64), (5, 6, 7, 3, 128), (9, 5, 3, 2, 64), (1, 1, 1, 1, 128),
+                 (21, 30, 52, 12, 128)]
+
+
+@pytest.mark.parametrize("T,H,W,heads,D", PERMUTE_CASES)
+def test_permute_bitexact(T, H, W, heads, D):
+    say(f"permute T={T} H={H} W={W} heads={heads} D={D}")
+    w = wl.custom(T, H, W, heads, D, cid=400)
+    q, _, _ = wl.qkv(w)
+    sh = _shape(w)
+    xd = bf16_to_dev(q)
+    tok = vsa.tile_permute(xd, sh, vsa.LAYOUT_TOKEN_MAJOR)
+    fea = vsa.tile_permute(xd, sh, vsa.LAYOUT_FEATURE_MAJOR)
+    back = vsa.tile_unpermute(tok, sh)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(tok), vo.permute(q, T, H, W))
+    assert np.array_equal(bits_of(fea), vo.permute(q, T, H, W, transposed=True))
+    assert np.array_equal(bits_of(back), q)
+    # unpermute of arbitrary tile contents (padded rows hold garbage)
+    rnd = np.random.default_rng(T + H + W).integers(0, 2 ** 16, size=bits_of(tok).shape,
+                                                    dtype=np.uint16)
+    out = vsa.tile_unpermute(bf16_to_dev(rnd), sh)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), vo.unpermute(rnd, T, H, W))
+
+
+# --------------------------------------------------------------------- mask
+
+MASK_CASES = [(0, 0), (1, 0), (2, 0), (2, 1), (2, 2), (2, 3), (2, 4), (3, 0), (4, 0), (4, 1)]
+
+
+@pytest.mark.parametrize("cid,ki", MASK_CASES)
+def test_mask_bitexact_workloads(cid, ki):
+    w = wl.WORKLOADS[cid]
+    kcount = w.dense_counts[ki]
+    say(f"mask {w.name} k={kcount}")
+    r, s = wl.radii_scores(w)
+    rp, ci, routed = vsa.build_mask(torch.from_numpy(r).to(dev()), torch.from_numpy(s).to(dev()),
+                                    _shape(w), kcount, max(w.radius_set))
+    torch.cuda.synchronize()
+    rp = rp.cpu().numpy().astype(np.int64)
+    nnz = int(rp[-1])
+    ci = ci[:nnz].cpu().numpy().astype(np.int64)
+    routed = routed.cpu().numpy()
+    n = w.n_cells
+    off = 0
+    for h in range(w.heads):  # per head to bound the oracle's memory
+        keep, rt = vo.block_mask(r[:, h:h + 1], s[:, h:h + 1], kcount, w.T, w.H, w.W)
+        orp, oci = vo.csr(keep)
+        assert np.array_equal(routed[0, h].astype(bool), rt[0, 0]), f"routed head {h}"
+        assert np.array_equal(rp[h * n:(h + 1) * n + 1] - rp[h * n], orp), f"row_ptr head {h}"
+        assert np.array_equal(ci[off:off + len(oci)], oci), f"col_idx head {h}"
+        off += len(oci)
+    assert off == nnz
+
+
+def test_mask_ties_nan_inf_and_clamp():
+    """Crafted scores with ties, signed zeros, infinities and NaN; radii above
+    r_max are clamped to r_max."""
+    T, H, W = 13, 9, 17
+    w = wl.custom(T, H, W, 3, 64, radius_set=(0, 1, 2, 3, 4, 5, 6), cid=401)
+    r, s = wl.radii_scores(w)
+    pool = np.array([0.25, 0.5, 0.5, -0.0, 0.0, np.inf, -np.inf, np.nan, -np.nan, 1.0], np.float32)
+    s = np.random.default_rng(5).choice(pool, size=s.shape).astype(np.float32)
+    for kcount in (0, 1, 7, 20, w.n_cells):
+        rp, ci, routed = vsa.build_mask(torch.from_numpy(r).to(dev()), torch.from_numpy(s).to(dev()),
+                                        _shape(w), kcount, 4)
+        torch.cuda.synchronize()
+        keep, rt = vo.block_mask(np.minimum(r, 4), s, kcount, T, H, W)
+        orp, oci = vo.csr(keep)
+        rp = rp.cpu().numpy()
+        assert np.array_equal(rp, orp)
+        assert np.array_equal(ci[: rp[-1]].cpu().numpy(), oci)
+        assert np.array_equal(routed.cpu().numpy().astype(bool), rt)
+
+
+# ------------------------------------------------------------- attention
+
+SMALL = [  # T, H, W, heads, D, radius set, routed counts
+    (8, 16, 16, 2, 64, (1, 2, 3), (6, 0, 32)),
+    (5, 6, 7, 2, 128, (0, 1, 2), (0, 1, 4)),
+    (9, 5, 3, 3, 64, (0, 1), (1,)),
+    (13, 9, 17, 2, 128, (1, 2, 3, 4), (0, 5, 60)),
+    (1, 1, 1, 1, 64, (0,), (0, 1)),
+    (12, 8, 8, 2, 128, (0,), (0,)),
+]
+
+
+@pytest.mark.parametrize("T,H,W,heads,D,rset,kset", SMALL)
+def test_attention_full_small(T, H, W, heads, D, rset, kset):
+    w = wl.custom(T, H, W, heads, D, radius_set=rset, cid=402)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    for kcount in kset:
+        say(f"attention T={T} H={H} W={W} heads={heads} D={D} k={kcount}")
+        out = _run_all(w, q, k, v, r, s, kcount)
+        ref, lse = vo.attention(q, k, v, r, s, kcount, T, H, W, w.scale)
+        assert_close(f64_of(out["o"]), ref, "O")
+        # LSE of valid rows, read through the token-major permute of the oracle
+        lse_t = out["lse"].cpu().numpy().astype(np.float64)          # [B, Hh, Npad]
+        lse_ref_t = vo.permute(lse.transpose(0, 2, 1)[..., None], T, H, W)[..., 0]
+        valid = vo.permute(np.ones((1, T * H * W, heads, 1)), T, H, W)[..., 0] > 0
+        d = np.abs(lse_t - lse_ref_t)[valid]
+        say(f"  LSE max_abs={d.max():.3e}")
+        assert d.max() <= LSE_ABS
+
+
+def test_attention_split_invariance_and_determinism():
+    w = wl.WORKLOADS[0]
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    kcount = w.dense_counts[0]
+    ref, _ = vo.attention(q, k, v, r, s, kcount, w.T, w.H, w.W, w.scale)
+    base = None
+    for chunk in (0, 1, 2, 5, 13):
+        say(f"attention {w.name} kv_chunk={chunk}")
+        out = _run_all(w, q, k, v, r, s, kcount, kv_chunk=chunk)
+        got = f64_of(out["o"])
+        assert_close(got, ref, f"O kv_chunk={chunk}")
+        again = _run_all(w, q, k, v, r, s, kcount, kv_chunk=chunk)
+        assert np.array_equal(bits_of(again["o"]), bits_of(out["o"])), "not deterministic"
+        if base is None:
+            base = got
+        else:
+            assert np.abs(got - base).max() <= 2e-2
+
+
+def _sample_tiles(w, r, s, kcount, h, rng, n_routed=4, n_edge=4, n_rand=8):
+    """Query tiles to check for head h: routed ones, edge (padded) ones, random."""
+    n = w.n_cells
+    routed = np.flatnonzero(vo.routed_tiles(s[0, h], kcount))
+    c = vo.tile_coords(w.T, w.H, w.W)
+    a, b, cc = vo.tile_grid(w.T, w.H, w.W)
+    edge = np.flatnonzero((4 * (c[:, 0] + 1) > w.T) | (4 * (c[:, 1] + 1) > w.H) |
+                          (4 * (c[:, 2] + 1) > w.W))
+    pick = []
+    for pool, m in ((routed, n_routed), (edge, n_edge), (np.arange(n), n_rand)):
+        if len(pool):
+            pick.extend(rng.choice(pool, size=min(m, len(pool)), replace=False).tolist())
+    return sorted(set(pick))
+
+
+def _check_sampled(w, q, k, v, r, s, kcount, out, heads, seed=0):
+    rng = np.random.default_rng(seed)
+    tt = vo.token_tile(w.T, w.H, w.W)
+    o = f64_of(out["o"])
+    got_all, ref_all = [], []
+    for h in heads:
+        keep = vo.tile_keep(r[0, h], vo.routed_tiles(s[0, h], kcount), w.T, w.H, w.W)
+        qf, kf, vf = (vo.bf16_to_f64(x[0, :, h]) for x in (q, k, v))
+        tiles = _sample_tiles(w, r, s, kcount, h, rng)
+        rows = np.flatnonzero(np.isin(tt, tiles))
+        ref, _ = vo.attention_head_rows(qf, kf, vf, keep, tt, rows, w.scale)
+        got_all.append(o[0, rows, h])
+        ref_all.append(ref)
+    assert_close(np.concatenate(got_all), np.concatenate(ref_all), f"{w.name} k={kcount} sampled")
+
+
+def test_attention_wan13b_sampled():
+    w = wl.WORKLOADS[1]
+    kcount = w.dense_counts[0]
+    say(f"attention {w.name} k={kcount} (generating inputs)")
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    out = _run_all(w, q, k, v, r, s, kcount)
+    _check_sampled(w, q, k, v, r, s, kcount, out, heads=[0, 5, 11])
+    # the CSR of the full-size call is exact too
+    keep, _ = vo.block_mask(r[:, :1], s[:, :1], kcount, w.T, w.H, w.W)
+    orp, oci = vo.csr(keep)
+    assert np.array_equal(out["rp"][: w.n_cells + 1].cpu().numpy(), orp)
+
+
+@pytest.mark.parametrize("cid,ki", [(2, 0), (2, 1), (2, 4), (3, 0), (4, 0), (4, 1)])
+def test_attention_large_sampled(cid, ki):
+    w = wl.WORKLOADS[cid]
+    kcount = w.dense_counts[ki]
+    say(f"attention {w.name} k={kcount} (generating inputs)")
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    out = _run_all(w, q, k, v, r, s, kcount)
+    _check_sampled(w, q, k, v, r, s, kcount, out, heads=[0, w.heads - 1], seed=cid)
+    del out
+    torch.cuda.empty_cache()

@@ -1,0 +1,117 @@
+"""Host-side checks of libvsa.so that need no GPU: the library loads, exports
+every entry point of include/vsa.h, and rejects bad arguments before
+enqueueing anything (no HIP call is reached on these paths)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+vsa = pytest.importorskip("block_sparse_attention_19_amd")
+
+INVALID, UNSUPPORTED, CAPACITY, OVERFLOW = 1, 2, 3, 4
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "vsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) >= 10
+    L = vsa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = vsa.lib()
+    for code in range(6):
+        assert L.vsa_status_string(code).decode()
+
+
+def test_num_tiles_and_bounds():
+    L = vsa.lib()
+    s = vsa.shape(1, 12, 128, 21, 30, 52)
+    assert vsa.num_tiles(s) == 6 * 8 * 13
+    bad = vsa.shape(1, 12, 128, 0, 30, 52)
+    assert L.vsa_num_tiles(ctypes.byref(bad)) == -1
+    assert L.vsa_mask_nnz_bound(ctypes.byref(s), 3, 700) == -1   # dense_count > nT
+    assert L.vsa_mask_nnz_bound(ctypes.byref(s), 256, 0) == -1   # r_max > 255
+    # all routed: every pair
+    assert vsa.mask_nnz_bound(s, 3, 624) == 12 * 624 * 624
+
+
+@pytest.mark.parametrize("T,H,W,rmax,k", [(8, 16, 16, 3, 6), (5, 6, 7, 2, 0), (21, 30, 52, 3, 125),
+                                          (9, 5, 3, 4, 3)])
+def test_nnz_bound_covers_oracle(T, H, W, rmax, k):
+    """The host bound is never below the exact count of kept pairs."""
+    import workloads as wl
+    from oracle import vsa_oracle as vo
+    w = wl.custom(T, H, W, 2, 64, radius_set=tuple(range(0, rmax + 1)), cid=300)
+    r, sc = wl.radii_scores(w)
+    r[:] = np.minimum(r, rmax)
+    keep, _ = vo.block_mask(r, sc, k, T, H, W)
+    nnz = int(keep.sum())
+    full = vo.block_mask(np.full_like(r, rmax), sc, k, T, H, W)[0].sum()
+    bound = vsa.mask_nnz_bound(vsa.shape(1, 2, 64, T, H, W), rmax, k)
+    assert bound >= full >= nnz
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+def test_validation_rejects_before_launch():
+    L = vsa.lib()
+    s = vsa.shape(1, 2, 64, 8, 16, 16)
+    sp = ctypes.byref(s)
+    good = _p(0x10000)
+    # permute: null / misaligned / bad layout
+    assert L.vsa_tile_permute(sp, None, good, 0, None) == INVALID
+    assert L.vsa_tile_permute(sp, _p(0x10008), good, 0, None) == INVALID
+    assert L.vsa_tile_permute(sp, good, good, 7, None) == INVALID
+    assert L.vsa_tile_unpermute(sp, good, None, None) == INVALID
+    # unsupported head_dim
+    s96 = vsa.shape(1, 2, 96, 8, 16, 16)
+    assert L.vsa_tile_permute(ctypes.byref(s96), good, good, 0, None) == UNSUPPORTED
+    assert L.vsa_tile_permute(None, good, good, 0, None) == INVALID
+    # mask: dense_count, r_max, capacity
+    nT = 32
+    cap = vsa.mask_nnz_bound(s, 3, 6)
+    assert L.vsa_build_mask(sp, good, good, nT + 1, 3, good, good, 10 ** 6, good, None, 0, None) == INVALID
+    assert L.vsa_build_mask(sp, good, good, 6, 300, good, good, 10 ** 6, good, None, 0, None) == INVALID
+    assert L.vsa_build_mask(sp, good, good, 6, 3, good, good, cap - 1, good, None, 0, None) == CAPACITY
+    assert L.vsa_build_mask(sp, good, good, 6, 3, good, good, cap, None, good, 0, None) == CAPACITY
+    assert L.vsa_build_mask(sp, good, _p(0x10002), 6, 3, good, good, cap, good, None, 0, None) == INVALID
+    # attention: scale, workspace, kv_chunk
+    ws = vsa.attn_workspace_bytes(s, 0)
+    assert ws > 0
+    assert L.vsa_attn_fwd(sp, good, good, good, good, good, 0.0, good, None, 0, good, ws, None) == INVALID
+    assert L.vsa_attn_fwd(sp, good, good, good, good, good, float("nan"), good, None, 0, good, ws, None) == INVALID
+    assert L.vsa_attn_fwd(sp, good, good, good, good, good, 0.125, good, None, -1, good, ws, None) == INVALID
+    assert L.vsa_attn_fwd(sp, good, good, good, good, good, 0.125, good, None, 0, good, ws - 1, None) == CAPACITY
+    assert L.vsa_attn_fwd(sp, good, good, good, good, good, 0.125, good, None, 0, _p(0x10010), ws, None) == INVALID
+    assert vsa.lib().vsa_last_error().decode()
+
+
+def test_overflow_is_reported():
+    L = vsa.lib()
+    # 16000 heads of a 2160-tile grid: 34.6M tile rows * 64 > int32
+    s = vsa.shape(1, 16000, 128, 33, 45, 80)
+    good = _p(0x10000)
+    assert L.vsa_tile_permute(ctypes.byref(s), good, good, 0, None) == OVERFLOW
+    s2 = vsa.shape(1, 600, 128, 33, 45, 80)   # dense bound 600*2160^2 > int32
+    cap = 2 ** 40
+    assert L.vsa_build_mask(ctypes.byref(s2), good, good, 2160, 4, good, good, cap, good, None, 0,
+                            None) == OVERFLOW
+
+
+def test_workspace_grows_with_split():
+    s = vsa.shape(1, 12, 128, 21, 30, 52)
+    assert vsa.attn_workspace_bytes(s, 1) > vsa.attn_workspace_bytes(s, 0) > 0

@@ -30,8 +30,10 @@ they are returned as uint16 bit patterns, token-raster order
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -160,6 +162,14 @@ def qkv(w: Workload, heads: Optional[range] = None):
     q = np.empty((1, N, len(hs), D), np.uint16)
     k = np.empty_like(q)
     v = np.empty_like(q)
-    for j, h in enumerate(hs):
+
+    def one(j_h):
+        j, h = j_h
         q[0, :, j], k[0, :, j], v[0, :, j] = head_qkv(w, h)
+
+    # heads are independent streams: draw them on a few threads (numpy's
+    # generators release the GIL while filling arrays)
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(hs)))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, enumerate(hs)))
     return q, k, v
