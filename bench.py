@@ -1,0 +1,216 @@
+"""Benchmark of one block-sparse video attention call on one MI355X.
+
+A step is the whole path over one batch of synthetic, HBM-resident input:
+tile permute of Q, K (token-major) and V (feature-major), CSR mask build from
+per-tile radii and routing scores, block-sparse attention forward (plan,
+flash kernel, split combine) and the unpermute of O.  Default workload: the
+Wan2.1-1.3B 480p-shaped call, 21x30x52 latent grid (32760 tokens), 12 heads,
+head_dim 128, radii in {1, 2, 3}, 20% of query tiles routed dense.
+
+Prints ONE JSON line.  ``value`` is retained-tile bf16 TFLOP/s of the whole
+step (kept tile pairs x 4*64*64*D flops over the step time); ``roofline``
+rates the attention kernel alone against the bf16 MFMA peak; ``cpu_baseline``
+times the fp64 CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "retained-tile bf16 TFLOP/s (% MFMA peak) + ms/attention call, 32760 tokens"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic_wan2.1-1.3b-480p.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_19_amd", "csrc", "attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--dense-index", type=int, default=0,
+                    help="which routed count of the workload's sweep")
+    ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
+    return ap.parse_args()
+
+
+def attn_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_figure(n_launch_units: float):
+    """HBM bytes per attention launch from committed rocprofv3 counters, or None
+    when they were taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_source_sha") != attn_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, r, s, kcount, budget_s):
+    """fp64 oracle on sampled query tiles of the same workload, until the time
+    budget is spent; rated in retained-tile TFLOP/s like the GPU."""
+    import numpy as np
+    from oracle import vsa_oracle as vo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(1234)
+    tt = vo.token_tile(w.T, w.H, w.W)
+    done_tiles, pairs, t0 = 0, 0, time.perf_counter()
+    heads = list(range(w.heads))
+    rng.shuffle(heads)
+    for h in heads:
+        keep = vo.tile_keep(r[0, h], vo.routed_tiles(s[0, h], kcount), w.T, w.H, w.W)
+        qf, kf, vf = (vo.bf16_to_f64(x[0, :, h]) for x in (q, k, v))
+        for a in rng.permutation(w.n_cells)[:8]:
+            rows = np.flatnonzero(tt == a)
+            vo.attention_head_rows(qf, kf, vf, keep, tt, rows, w.scale)
+            done_tiles += 1
+            pairs += int(keep[a].sum())
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = pairs * 4.0 * 64 * 64 * w.D
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done_tiles} query tiles ({pairs} retained tile pairs) of {w.name}, "
+                      f"fp64 masked attention over all keys, {el:.1f} s; full-call "
+                      f"extrapolation {el / max(done_tiles, 1) * w.heads * w.n_cells:.0f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_19_amd as vsa
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    kcount = w.dense_counts[args.dense_index]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    rd, sd = torch.from_numpy(r).to(dev), torch.from_numpy(s).to(dev)
+    sh = vsa.shape(w.batch, w.heads, w.D, w.T, w.H, w.W)
+    nT = w.n_cells
+    r_max = max(w.radius_set)
+    # every buffer is allocated before the timed region
+    q_t = torch.empty((1, w.heads, nT * 64, w.D), dtype=torch.bfloat16, device=dev)
+    k_t = torch.empty_like(q_t)
+    v_t = torch.empty((1, w.heads, nT, w.D, 64), dtype=torch.bfloat16, device=dev)
+    o_t = torch.empty_like(q_t)
+    lse = torch.empty((1, w.heads, nT * 64), dtype=torch.float32, device=dev)
+    o = torch.empty_like(qd)
+    mbuf = vsa.mask_buffers(sh, kcount, r_max, dev)
+    ws = torch.empty(vsa.attn_workspace_bytes(sh, args.kv_chunk), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    stages = ["permute_qkv", "mask", "attn", "unpermute"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        vsa.tile_permute(qd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=q_t)
+        vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=k_t)
+        vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR, out=v_t)
+        mark(1)
+        rp, ci, _ = vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf)
+        mark(2)
+        vsa.attn_fwd(q_t, k_t, v_t, rp, ci, sh, w.scale, args.kv_chunk, out=o_t, workspace=ws,
+                     lse_out=lse)
+        mark(3)
+        vsa.tile_unpermute(o_t, sh, out=o)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_all0.elapsed_time(t_all1) / args.steps
+    per_stage = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                 for j, n in enumerate(stages)}
+    nnz = int(mbuf[0][-1].item())
+    flops = nnz * 4.0 * 64 * 64 * w.D
+    # valid-token flops: each kept pair weighted by valid queries x valid keys
+    rp_h = mbuf[0].cpu().numpy().astype(np.int64)
+    ci_h = mbuf[1][:nnz].cpu().numpy().astype(np.int64)
+    a, b, c = w.grid_cells
+    per = [np.minimum(4, n - 4 * np.arange(m)) for n, m in ((w.T, a), (w.H, b), (w.W, c))]
+    valid = (per[0][:, None, None] * per[1][None, :, None] * per[2][None, None, :]).ravel()
+    row_tile = np.repeat(np.arange(len(rp_h) - 1) % nT, np.diff(rp_h))
+    valid_flops = 4.0 * w.D * float(np.sum(valid[row_tile] * valid[ci_h]))
+    attn_ms = per_stage["attn"]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Wan/HunyuanVideo-shaped Q/K/V, radii, routing scores)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "W": w.W, "tokens": w.tokens,
+                   "heads": w.heads, "head_dim": w.D, "batch": w.batch, "tiles": nT,
+                   "radius_set": list(w.radius_set), "dense_count": kcount,
+                   "retained_tile_pairs": nnz, "tile_pair_density": round(nnz / (w.heads * nT * nT), 4),
+                   "kv_chunk": args.kv_chunk, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_figure(1.0),
+                     "kernel": "vsa_attn_fwd (plan + attn_kernel + combine_kernel)"},
+        "breakdown_ms": {k2: round(v2, 4) for k2, v2 in per_stage.items()},
+        "attn_valid_token_tflops": round(valid_flops / (attn_ms * 1e-3) / 1e12, 2),
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, r, s, kcount, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -143,29 +143,41 @@ def mask_nnz_bound(s: Shape, r_max: int, dense_count: int) -> int:
     return n
 
 
+def mask_buffers(s: Shape, dense_count: int, r_max: int, device) -> Tuple[torch.Tensor, ...]:
+    """Preallocated (row_ptr, col_idx, routed) for build_mask(out=...)."""
+    nT = num_tiles(s)
+    cap = mask_nnz_bound(s, r_max, dense_count)
+    rows = s.batch * s.heads * nT
+    return (torch.empty(rows + 1, dtype=torch.int32, device=device),
+            torch.empty(max(cap, 1), dtype=torch.int32, device=device),
+            torch.empty((s.batch, s.heads, nT), dtype=torch.uint8, device=device))
+
+
 def build_mask(radii: torch.Tensor, scores: torch.Tensor, s: Shape, dense_count: int,
-               r_max: Optional[int] = None, with_routed: bool = True):
+               r_max: Optional[int] = None, with_routed: bool = True, out=None):
     """uint8 radii / float32 scores [B, heads, nT] -> (row_ptr int32 [rows+1],
     col_idx int32 [capacity], routed uint8 [B, heads, nT] or None).
 
-    ``r_max`` defaults to 255 (capacity for full rows)."""
+    ``r_max`` defaults to 255 (capacity for full rows).  ``out`` may pass the
+    three buffers of ``mask_buffers``."""
     radii = _require(radii, torch.uint8, "radii")
     scores = _require(scores, torch.float32, "scores")
     nT = num_tiles(s)
     if radii.shape != (s.batch, s.heads, nT) or scores.shape != (s.batch, s.heads, nT):
         raise ValueError("radii / scores must be [B, heads, nT]")
     r_max = 255 if r_max is None else int(r_max)
-    cap = mask_nnz_bound(s, r_max, dense_count)
     dev = radii.device
-    rows = s.batch * s.heads * nT
-    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
-    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
-    routed = torch.empty((s.batch, s.heads, nT), dtype=torch.uint8, device=dev) if with_routed else None
+    if out is None:
+        row_ptr, col_idx, routed = mask_buffers(s, dense_count, r_max, dev)
+        if not with_routed:
+            routed = None
+    else:
+        row_ptr, col_idx, routed = out
     ws_bytes = lib().vsa_mask_workspace_bytes(ctypes.byref(s))
-    ws = None if with_routed else torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = None if routed is not None else torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     _check(lib().vsa_build_mask(ctypes.byref(s), _ptr(radii), _ptr(scores), dense_count, r_max,
-                                _ptr(row_ptr), _ptr(col_idx), cap, _ptr(routed), _ptr(ws),
-                                ws_bytes if ws is not None else 0, _stream(dev)),
+                                _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(routed),
+                                _ptr(ws), ws_bytes if ws is not None else 0, _stream(dev)),
            "vsa_build_mask")
     return row_ptr, col_idx, routed
 
@@ -177,7 +189,8 @@ def attn_workspace_bytes(s: Shape, kv_chunk: int = 0) -> int:
 def attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: torch.Tensor,
              col_idx: torch.Tensor, s: Shape, scale: Optional[float] = None, kv_chunk: int = 0,
              with_lse: bool = True, out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             workspace: Optional[torch.Tensor] = None,
+             lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Tile-major q/k [B, heads, nT*64, D], feature-major v [B, heads, nT, D, 64]
     + CSR -> (o_t bf16 [B, heads, nT*64, D], lse float32 [B, heads, nT*64])."""
     q_t = _require(q_t, torch.bfloat16, "q_t")
@@ -196,7 +209,9 @@ def attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: t
     dev = q_t.device
     if out is None:
         out = torch.empty(tok, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(tok[:3], dtype=torch.float32, device=dev) if with_lse else None
+    lse = lse_out
+    if lse is None and with_lse:
+        lse = torch.empty(tok[:3], dtype=torch.float32, device=dev)
     ws_bytes = attn_workspace_bytes(s, kv_chunk)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

@@ -41,6 +41,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte chunk (native vector)
 
 constexpr int kThreads = 256;
 constexpr int kPlanThreads = 1024;
@@ -48,6 +49,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
 constexpr int kMinChunk = 32;          // smallest automatic key chunk (tiles)
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0), expcnt/lgkmcnt unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
 // Automatic splitting aims at this many G units (4x the resident workgroups of
 // a 256-CU part at 2 workgroups per CU); fixed so workspace sizes do not depend
 // on the device.
@@ -329,6 +332,10 @@ struct AttnArgs {
   float c2;            // scale * log2(e)
 };
 
+// Broadcast a wave-uniform value to a scalar register (the compiler cannot
+// prove uniformity of values derived from the thread index or read from LDS).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Row index of the K operand for A-operand row rho: bits 2 and 3 swapped.
 __device__ __forceinline__ int sigma(int rho) {
   return (rho & 0x13) | ((rho & 4) << 1) | ((rho & 8) >> 1);
@@ -339,7 +346,9 @@ struct Cfg {
   static constexpr int kRowBytes = D * 2;             // K row in LDS
   static constexpr int kChunks = D / 8;               // 16-byte chunks per K row
   static constexpr int kTileBytes = kTileTokens * D * 2;
-  static constexpr int kSlotBytes = 2 * kTileBytes;   // K + V^T
+  static constexpr int kTileChunks = kTileBytes / 16;
+  static constexpr int kSplitBytes = 2 * kTileBytes;  // K + V^T buffers of one key split
+  static constexpr int kLdsBytes = 2 * kSplitBytes;   // two key splits
   static constexpr int kKSteps = D / 16;              // k-steps of Q.K^T
   static constexpr int kDBlocks = D / 32;             // 32-row blocks of O^T
 };
@@ -353,20 +362,65 @@ __device__ __forceinline__ int k_off(int row, int c) {
 // LDS byte offset of 16-byte chunk c (8 keys) of V^T row d (swizzled).
 __device__ __forceinline__ int v_off(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
 
-// Copy one K tile and one V^T tile into an LDS slot, `nthr` threads starting
-// at thread index `t0` of the workgroup.
-template <int D>
-__device__ __forceinline__ void stage_tile(char* slot, const uint4* kt, const uint4* vt, int tid,
-                                           int nthr) {
-  constexpr int kChunksPerTile = Cfg<D>::kTileBytes / 16;
-  for (int i = tid; i < kChunksPerTile; i += nthr) {
-    const uint4 kv = kt[i];
-    const uint4 vv = vt[i];
-    const int kr = i / Cfg<D>::kChunks, kc = i % Cfg<D>::kChunks;
-    *reinterpret_cast<uint4*>(slot + k_off<D>(kr, kc)) = kv;
-    const int vr = i >> 3, vc = i & 7;
-    *reinterpret_cast<uint4*>(slot + Cfg<D>::kTileBytes + v_off(vr, vc)) = vv;
+// Workgroup barrier for LDS hand-offs: completes this wave's LDS operations,
+// then waits for every wave.  Unlike __syncthreads() it does not drain
+// outstanding global loads, so tile prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// NTHR threads move one 64 x D bf16 tile (K or V^T) from global memory to LDS
+// in 16-byte chunks; the loads are issued first and stored later, so the copy
+// overlaps compute.  Thread t owns chunks t + c*NTHR (global order); the tile
+// base is wave-uniform, so the loads use a scalar base plus one per-thread
+// offset, and the LDS addresses of all chunks of a thread differ by
+// compile-time constants (the swizzle period divides the rows between them).
+template <int D, int NTHR>
+struct Stage {
+  static constexpr int kN = Cfg<D>::kTileChunks / NTHR;
+  // K tile rows advanced by one chunk step of NTHR chunks
+  static constexpr int kKRowStep = NTHR / Cfg<D>::kChunks;
+  // V^T rows (8 chunks each) advanced by one chunk step
+  static constexpr int kVRowStep = NTHR / 8;
+};
+
+template <int NTHR, int N, int M>
+__device__ __forceinline__ void stage_load(u32x4 (&r)[M], const char* tile, int t) {
+  const char* p = tile + 16 * t;
+#pragma unroll
+  for (int c = 0; c < N; ++c) r[c] = *reinterpret_cast<const u32x4*>(p + c * NTHR * 16);
+}
+
+// The K swizzle has a period of 16 rows (D = 128) or 16 rows (D = 64, two
+// rows per 8-chunk pattern); chunk steps of a multiple of 16 rows keep it.
+template <int D, int NTHR, int N, int M>
+__device__ __forceinline__ void stage_store_k(const u32x4 (&r)[M], char* buf, int t) {
+  constexpr int step = Stage<D, NTHR>::kKRowStep;
+  if constexpr (step % 16 == 0) {
+    char* p = buf + k_off<D>(t / Cfg<D>::kChunks, t % Cfg<D>::kChunks);
+#pragma unroll
+    for (int c = 0; c < N; ++c)
+      *reinterpret_cast<u32x4*>(p + c * step * Cfg<D>::kRowBytes) = r[c];
+  } else {
+    static_assert(16 % step == 0, "staging row step");
+    constexpr int kPer = 16 / step;  // chunk steps per swizzle period
+#pragma unroll
+    for (int c0 = 0; c0 < kPer && c0 < N; ++c0) {
+      char* p = buf + k_off<D>(t / Cfg<D>::kChunks + c0 * step, t % Cfg<D>::kChunks);
+#pragma unroll
+      for (int c = c0; c < N; c += kPer)
+        *reinterpret_cast<u32x4*>(p + (c - c0) * step * Cfg<D>::kRowBytes) = r[c];
+    }
   }
+}
+
+template <int NTHR, int N, int M>
+__device__ __forceinline__ void stage_store_v(const u32x4 (&r)[M], char* buf, int t) {
+  constexpr int step = NTHR / 8;  // V^T rows per chunk step
+  static_assert(step % 16 == 0, "V swizzle period");
+  char* p = buf + v_off(t >> 3, t & 7);
+#pragma unroll
+  for (int c = 0; c < N; ++c) *reinterpret_cast<u32x4*>(p + c * step * 128) = r[c];
 }
 
 template <int D>
@@ -377,39 +431,46 @@ struct WaveState {
   float l;  // this lane's partial sum of P
 };
 
+// S^T (32 keys of half `kb` x 32 queries) = K Q^T for this wave's 32 rows.
 template <int D>
-__device__ __forceinline__ void process_tile(WaveState<D>& st, const char* slot, int lane,
-                                             uint64_t vmask, float c2) {
+__device__ __forceinline__ f32x16 qk_half(const char* kbuf, const WaveState<D>& st, int kb,
+                                          int lane) {
   const int q = lane & 31, h = lane >> 5;
-  f32x16 s[2];
+  const int krow = 32 * kb + sigma(q);
+  f32x16 s;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-  const int krow0 = sigma(q);
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
   for (int t = 0; t < Cfg<D>::kKSteps; ++t) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + k_off<D>(32 * kb + krow0, 2 * t + h));
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[t], s[kb], 0, 0, 0);
-    }
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + k_off<D>(krow, 2 * t + h));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[t], s, 0, 0, 0);
   }
-  // key index of register r of block kb in this lane: 32kb + 16(r/8) + 8h + r%8
-  if (vmask != ~0ull) {
+  return s;
+}
+
+// Valid-slot bits of this lane's 32 scores (bit 16*kb + r <-> register r of
+// half kb; key 32kb + 16(r/8) + 8h + r%8), from the tile's 64-bit mask.
+__device__ __forceinline__ uint32_t lane_bits(uint64_t vmask, int h) {
+  const uint32_t lo = (uint32_t)vmask, hi = (uint32_t)(vmask >> 32);
+  const int sh = 8 * h;
+  return ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) | (((hi >> sh) & 0xffu) << 16) |
+         (((hi >> (16 + sh)) & 0xffu) << 24);
+}
+
+// Online softmax of the 32 scores of half `kb` and O^T += V^T P^T over them.
+template <int D>
+__device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, const char* vbuf,
+                                                int kb, int lane, bool edge, uint32_t bits,
+                                                float c2) {
+  const int q = lane & 31, h = lane >> 5;
+  if (edge) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
-        if (!((vmask >> key) & 1ull)) s[kb][r] = -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r)
+      if (!((bits >> (16 * kb + r)) & 1u)) s[r] = -INFINITY;
   }
-  float mx = s[0][0];
+  float mx = s[0];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float mc = mx * c2;
   if (__any(mc > st.m + kRescaleSlack)) {
@@ -423,27 +484,82 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const char* slot,
     st.m = mn;
   }
   const float mneg = (st.m == -INFINITY) ? 0.f : -st.m;
-  bf16x8 pb[2][2];
+  bf16x8 pb[2];
   float lsum = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, mneg));
-      lsum += pv;
-      pb[kb][r >> 3][r & 7] = (__bf16)pv;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c2, mneg));
+    lsum += pv;
+    pb[r >> 3][r & 7] = (__bf16)pv;
+  }
   st.l += lsum;
 #pragma unroll
-  for (int db = 0; db < Cfg<D>::kDBlocks; ++db) {
+  for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            slot + Cfg<D>::kTileBytes + v_off(32 * db + q, 4 * kb + 2 * s2 + h));
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][s2], st.o[db], 0, 0, 0);
-      }
+    for (int db = 0; db < Cfg<D>::kDBlocks; ++db) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(vbuf + v_off(32 * db + q, 4 * kb + 2 * s2 + h));
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], st.o[db], 0, 0, 0);
+    }
+}
+
+// Walk the key tiles of a unit.  SPLIT = false: all 4 waves share each tile
+// (two query tiles x two 32-row halves).  SPLIT = true: waves 0-1 take the
+// even positions of the key list and waves 2-3 the odd ones (one query tile).
+// Each step: prefetch the next K tile, S = K Q^T, barrier, store next K and
+// prefetch next V, softmax + PV, barrier, store next V.
+template <int D, bool SPLIT, int M>
+__device__ __forceinline__ void run_steps(WaveState<D>& st, u32x4 (&rs)[M],
+                                          char* smem, const int* cols, int nkeys,
+                                          const char* kbase, const char* vbase, const AttnArgs& a,
+                                          int tid, int lane, int grp) {
+  constexpr int NTHR = SPLIT ? 128 : kThreads;
+  constexpr int KN = Stage<D, NTHR>::kN;
+  static_assert(KN <= M, "staging registers");
+  constexpr int STRIDE = SPLIT ? 2 : 1;
+  constexpr int TB = Cfg<D>::kTileBytes;
+  const int t = SPLIT ? (tid & 127) : tid;
+  const int my = SPLIT ? grp : 0;
+  char* kbuf = smem + my * Cfg<D>::kSplitBytes;
+  char* vbuf = kbuf + Cfg<D>::kTileBytes;
+  const int nsteps = SPLIT ? (nkeys + 1) / 2 : nkeys;
+  const int h = lane >> 5;
+  int j = (my < nkeys) ? uni(cols[my]) : -1;
+  int jn = (STRIDE + my < nkeys) ? uni(cols[STRIDE + my]) : -1;
+  // One set of staging registers carries the next K tile during Q.K^T and
+  // then the next V tile during softmax + P.V.
+  if (j >= 0) {
+    stage_load<NTHR, KN>(rs, kbase + (int64_t)j * TB, t);
+    stage_store_k<D, NTHR, KN>(rs, kbuf, t);
+    stage_load<NTHR, KN>(rs, vbase + (int64_t)j * TB, t);
+    stage_store_v<NTHR, KN>(rs, vbuf, t);
+  }
+  lds_barrier();
+  for (int step = 0; step < nsteps; ++step) {
+    const int pnn = (step + 2) * STRIDE + my;
+    const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;  // made uniform one step later
+    if (jn >= 0) stage_load<NTHR, KN>(rs, kbase + (int64_t)jn * TB, t);
+    // The tile is consumed in two halves of 32 keys (halves the score and P
+    // registers); the K buffer is free once the second half's scores exist.
+    const uint64_t vm = (j >= 0) ? tile_valid_mask(j, a.nh, a.nw, a.T, a.H, a.W) : ~0ull;
+    const bool edge = vm != ~0ull;
+    const uint32_t bits = lane_bits(vm, h);
+    f32x16 s1;
+    if (j >= 0) {
+      const f32x16 s0 = qk_half<D>(kbuf, st, 0, lane);
+      softmax_pv_half<D>(st, s0, vbuf, 0, lane, edge, bits, a.c2);
+      s1 = qk_half<D>(kbuf, st, 1, lane);
+    }
+    lds_barrier();
+    if (jn >= 0) {
+      stage_store_k<D, NTHR, KN>(rs, kbuf, t);
+      stage_load<NTHR, KN>(rs, vbase + (int64_t)jn * TB, t);
+    }
+    if (j >= 0) softmax_pv_half<D>(st, s1, vbuf, 1, lane, edge, bits, a.c2);
+    lds_barrier();
+    if (jn >= 0) stage_store_v<NTHR, KN>(rs, vbuf, t);
+    j = jn;
+    jn = uni(jnn_v);
   }
 }
 
@@ -451,25 +567,33 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_unit;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
   const int q = lane & 31, h = lane >> 5;
   const int nT = args.nT;
   const int n_units = args.hdr->n_units;
-  const float c2 = args.c2;
+  const int half = wave & 1;
+  const int grp = wave >> 1;  // G: which query tile; S: which key split
+  constexpr int TC = Cfg<D>::kTileChunks;
+  // staging registers shared by both unit kinds (sized for the split kind)
+  u32x4 rs[Stage<D, 128>::kN];
 
   for (;;) {
     if (tid == 0) s_unit = atomicAdd(&args.hdr_mut->counter, 1);
-    __syncthreads();
-    const int ui = s_unit;
-    __syncthreads();
+    lds_barrier();
+    const int ui = uni(s_unit);
+    lds_barrier();
     if (ui >= n_units) break;
-    const Unit u = args.units[ui];
+    Unit u = args.units[ui];
+    u.row[0] = uni(u.row[0]);
+    u.row[1] = uni(u.row[1]);
+    u.kb = uni(u.kb);
+    u.ke = uni(u.ke);
+    u.slot = uni(u.slot);
+    u.mode = uni(u.mode);
     const bool g_mode = (u.mode == 0);
-    const int half = wave & 1;
-    const int grp = wave >> 1;            // G: which query tile; S: which key split
-    const int row = g_mode ? u.row[grp] : u.row[0];
+    const int row = (g_mode && grp) ? u.row[1] : u.row[0];
     const int64_t bh = row / nT;
-    const int64_t qrow0 = (int64_t)row * kTileTokens + 32 * half;  // == (bh*nT + a)*64 + 32*half
+    const int64_t qrow0 = (int64_t)row * kTileTokens + 32 * half;
 
     WaveState<D> st;
     {
@@ -477,6 +601,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
 #pragma unroll
       for (int t = 0; t < Cfg<D>::kKSteps; ++t)
         st.qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
+      // Q must be complete before the key loop: otherwise the wait counts the
+      // compiler derives inside the loop also cover the tile prefetches and
+      // stall Q.K^T on them.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 #pragma unroll
     for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
@@ -485,37 +613,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     st.m = -INFINITY;
     st.l = 0.f;
 
-    const int cbase = args.row_ptr[u.row[0]];
+    const int* cols = args.col_idx + uni(args.row_ptr[u.row[0]]) + u.kb;
     const int nkeys = u.ke - u.kb;
-    const int nsteps = g_mode ? nkeys : (nkeys + 1) / 2;
-    const uint4* kbase = reinterpret_cast<const uint4*>(args.k + bh * (int64_t)nT * kTileTokens * D);
-    const uint4* vbase = reinterpret_cast<const uint4*>(args.v + bh * (int64_t)nT * kTileTokens * D);
-    constexpr int kTileChunks = Cfg<D>::kTileBytes / 16;
-
-    for (int step = 0; step < nsteps; ++step) {
-      // stage this step's tile(s)
-      int my_tile = -1;
-      if (g_mode) {
-        const int j = args.col_idx[cbase + u.kb + step];
-        stage_tile<D>(smem, kbase + (int64_t)j * kTileChunks, vbase + (int64_t)j * kTileChunks, tid,
-                      kThreads);
-        my_tile = j;
-      } else {
-        const int pos = u.kb + 2 * step + grp;
-        if (pos < u.ke) {
-          const int j = args.col_idx[cbase + pos];
-          stage_tile<D>(smem + grp * Cfg<D>::kSlotBytes, kbase + (int64_t)j * kTileChunks,
-                        vbase + (int64_t)j * kTileChunks, tid & 127, 128);
-          my_tile = j;
-        }
-      }
-      __syncthreads();
-      if (my_tile >= 0) {
-        const uint64_t vm = tile_valid_mask(my_tile, args.nh, args.nw, args.T, args.H, args.W);
-        process_tile<D>(st, smem + (g_mode ? 0 : grp * Cfg<D>::kSlotBytes), lane, vm, c2);
-      }
-      __syncthreads();
-    }
+    const char* kbase = reinterpret_cast<const char*>(args.k) + bh * (int64_t)nT * TC * 16;
+    const char* vbase = reinterpret_cast<const char*>(args.v) + bh * (int64_t)nT * TC * 16;
+    if (g_mode)
+      run_steps<D, false>(st, rs, smem, cols, nkeys, kbase, vbase, args, tid, lane, grp);
+    else
+      run_steps<D, true>(st, rs, smem, cols, nkeys, kbase, vbase, args, tid, lane, grp);
 
     // S units: merge the two key splits (waves 2,3 -> waves 0,1) through LDS.
     if (!g_mode) {
@@ -528,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
         xo[Cfg<D>::kDBlocks * 16 * 64 + lane] = st.m;
         xo[(Cfg<D>::kDBlocks * 16 + 1) * 64 + lane] = st.l;
       }
-      __syncthreads();
+      lds_barrier();
       if (grp == 0) {
         const float m1 = xo[Cfg<D>::kDBlocks * 16 * 64 + lane];
         const float l1 = xo[(Cfg<D>::kDBlocks * 16 + 1) * 64 + lane];
@@ -543,7 +648,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
         st.l = w0 * st.l + w1 * l1;
         st.m = mm;
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     const bool writer = g_mode || grp == 0;
@@ -674,11 +779,11 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   aa.c2 = scale * kLog2e;
   const int grid = (int)std::min<int64_t>(L.max_units, 2LL * cus);
   if (s.head_dim == 128) {
-    const size_t lds = 2 * Cfg<128>::kSlotBytes;
+    const size_t lds = Cfg<128>::kLdsBytes;
     attn_kernel<128><<<grid, kThreads, lds, stream>>>(aa);
     combine_kernel<128><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
   } else {
-    const size_t lds = 2 * Cfg<64>::kSlotBytes;
+    const size_t lds = Cfg<64>::kLdsBytes;
     attn_kernel<64><<<grid, kThreads, lds, stream>>>(aa);
     combine_kernel<64><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
   }
@@ -687,10 +792,10 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
 
 hipError_t attn_set_lds_limits() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<128>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Cfg<128>::kSlotBytes);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<128>::kLdsBytes);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<64>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Cfg<64>::kSlotBytes);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<64>::kLdsBytes);
 }
 
 }  // namespace vsa
