@@ -34,9 +34,16 @@ COMMON = [
 ]
 
 
+# Device-only flags per source: the attention kernel treats NaN as absent
+# (scores are finite or -inf), which lets max/min skip NaN canonicalisation.
+DEVICE_FLAGS = {
+    "attn.hip": ["-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

@@ -369,60 +369,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// NTHR threads move one 64 x D bf16 tile (K or V^T) from global memory to LDS
-// in 16-byte chunks; the loads are issued first and stored later, so the copy
-// overlaps compute.  Thread t owns chunks t + c*NTHR (global order); the tile
-// base is wave-uniform, so the loads use a scalar base plus one per-thread
-// offset, and the LDS addresses of all chunks of a thread differ by
-// compile-time constants (the swizzle period divides the rows between them).
-template <int D, int NTHR>
-struct Stage {
-  static constexpr int kN = Cfg<D>::kTileChunks / NTHR;
-  // K tile rows advanced by one chunk step of NTHR chunks
-  static constexpr int kKRowStep = NTHR / Cfg<D>::kChunks;
-  // V^T rows (8 chunks each) advanced by one chunk step
-  static constexpr int kVRowStep = NTHR / 8;
-};
-
-template <int NTHR, int N, int M>
-__device__ __forceinline__ void stage_load(u32x4 (&r)[M], const char* tile, int t) {
-  const char* p = tile + 16 * t;
-#pragma unroll
-  for (int c = 0; c < N; ++c) r[c] = *reinterpret_cast<const u32x4*>(p + c * NTHR * 16);
-}
-
-// The K swizzle has a period of 16 rows (D = 128) or 16 rows (D = 64, two
-// rows per 8-chunk pattern); chunk steps of a multiple of 16 rows keep it.
-template <int D, int NTHR, int N, int M>
-__device__ __forceinline__ void stage_store_k(const u32x4 (&r)[M], char* buf, int t) {
-  constexpr int step = Stage<D, NTHR>::kKRowStep;
-  if constexpr (step % 16 == 0) {
-    char* p = buf + k_off<D>(t / Cfg<D>::kChunks, t % Cfg<D>::kChunks);
-#pragma unroll
-    for (int c = 0; c < N; ++c)
-      *reinterpret_cast<u32x4*>(p + c * step * Cfg<D>::kRowBytes) = r[c];
-  } else {
-    static_assert(16 % step == 0, "staging row step");
-    constexpr int kPer = 16 / step;  // chunk steps per swizzle period
-#pragma unroll
-    for (int c0 = 0; c0 < kPer && c0 < N; ++c0) {
-      char* p = buf + k_off<D>(t / Cfg<D>::kChunks + c0 * step, t % Cfg<D>::kChunks);
-#pragma unroll
-      for (int c = c0; c < N; c += kPer)
-        *reinterpret_cast<u32x4*>(p + (c - c0) * step * Cfg<D>::kRowBytes) = r[c];
-    }
-  }
-}
-
-template <int NTHR, int N, int M>
-__device__ __forceinline__ void stage_store_v(const u32x4 (&r)[M], char* buf, int t) {
-  constexpr int step = NTHR / 8;  // V^T rows per chunk step
-  static_assert(step % 16 == 0, "V swizzle period");
-  char* p = buf + v_off(t >> 3, t & 7);
-#pragma unroll
-  for (int c = 0; c < N; ++c) *reinterpret_cast<u32x4*>(p + c * step * 128) = r[c];
-}
-
 template <int D>
 struct WaveState {
   bf16x8 qreg[Cfg<D>::kKSteps];
@@ -431,47 +377,81 @@ struct WaveState {
   float l;  // this lane's partial sum of P
 };
 
-// S^T (32 keys of half `kb` x 32 queries) = K Q^T for this wave's 32 rows.
+// S^T (32 keys x 32 queries) = K Q^T for this wave's 32 query rows, from a
+// block of 32 consecutive K rows (`k32`: row i of the block at i * 2D bytes,
+// swizzled as k_off).
 template <int D>
-__device__ __forceinline__ f32x16 qk_half(const char* kbuf, const WaveState<D>& st, int kb,
-                                          int lane) {
+__device__ __forceinline__ f32x16 qk32(const char* k32, const WaveState<D>& st, int lane) {
   const int q = lane & 31, h = lane >> 5;
-  const int krow = 32 * kb + sigma(q);
+  const int krow = sigma(q);
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
   for (int t = 0; t < Cfg<D>::kKSteps; ++t) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + k_off<D>(krow, 2 * t + h));
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(k32 + k_off<D>(krow, 2 * t + h));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[t], s, 0, 0, 0);
   }
   return s;
 }
 
-// Valid-slot bits of this lane's 32 scores (bit 16*kb + r <-> register r of
-// half kb; key 32kb + 16(r/8) + 8h + r%8), from the tile's 64-bit mask.
-__device__ __forceinline__ uint32_t lane_bits(uint64_t vmask, int h) {
-  const uint32_t lo = (uint32_t)vmask, hi = (uint32_t)(vmask >> 32);
-  const int sh = 8 * h;
-  return ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) | (((hi >> sh) & 0xffu) << 16) |
-         (((hi >> (16 + sh)) & 0xffu) << 24);
+// LDS byte offset of 16-byte chunk c4 (8 keys) of row d of a half V^T tile
+// (32 keys per row, 64 bytes; swizzled so 16 consecutive rows hit 16 distinct
+// bank groups).
+__device__ __forceinline__ int vh_off(int d, int c4) { return d * 64 + ((c4 ^ ((d >> 2) & 3)) << 4); }
+
+// Extent of a key tile inside the grid (tokens valid along t, h, w); a tile
+// with any extent below 4 holds padding slots that must not be attended.
+struct TileExtent {
+  int vt, vh, vw;
+  bool edge;
+};
+
+__device__ __forceinline__ TileExtent tile_extent(int tau, int nh, int nw, int T, int H, int W) {
+  TileExtent e;
+  const int tw = tau % nw, th = (tau / nw) % nh, tt = tau / (nw * nh);
+  e.vt = min(kTile, T - tt * kTile);
+  e.vh = min(kTile, H - th * kTile);
+  e.vw = min(kTile, W - tw * kTile);
+  e.edge = (e.vt < kTile) | (e.vh < kTile) | (e.vw < kTile);
+  return e;
+}
+
+// Values of lane l and lane l ^ 32 combined (v_permlane32_swap exchanges the
+// two 32-lane halves; with the same register on both sides, the pair of
+// results holds both halves' values in every lane).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Online softmax of the 32 scores of half `kb` and O^T += V^T P^T over them.
-template <int D>
+// Register r of half kb in lane (q, h) holds key slot 32kb + 16(r/8) + 8h + r%8,
+// i.e. lt = 2kb + r/8, lh = 2h + (r/4)%2, lw = r%4.
+// HALF_V: `vbuf` holds only the 32 keys of this half ([D][32], vh_off);
+// otherwise the whole tile ([D][64], v_off).
+template <int D, bool HALF_V>
 __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, const char* vbuf,
-                                                int kb, int lane, bool edge, uint32_t bits,
+                                                int kb, int lane, const TileExtent& ext,
                                                 float c2) {
   const int q = lane & 31, h = lane >> 5;
-  if (edge) {
+  if (ext.edge) {
+    const bool h_ok0 = 2 * h < ext.vh, h_ok1 = 2 * h + 1 < ext.vh;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (!((bits >> (16 * kb + r)) & 1u)) s[r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const bool tw_ok = ((2 * kb + (r >> 3)) < ext.vt) && ((r & 3) < ext.vw);
+      const bool ok = tw_ok && ((r & 4) ? h_ok1 : h_ok0);
+      s[r] = ok ? s[r] : -INFINITY;
+    }
   }
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_halves(mx);
   const float mc = mx * c2;
   if (__any(mc > st.m + kRescaleSlack)) {
     const float mn = fmaxf(st.m, mc);
@@ -483,7 +463,8 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
       for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     st.m = mn;
   }
-  const float mneg = (st.m == -INFINITY) ? 0.f : -st.m;
+  // every tile holds at least one valid key, so the running max is finite here
+  const float mneg = -st.m;
   bf16x8 pb[2];
   float lsum = 0.f;
 #pragma unroll
@@ -497,67 +478,171 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int db = 0; db < Cfg<D>::kDBlocks; ++db) {
-      const bf16x8 a =
-          *reinterpret_cast<const bf16x8*>(vbuf + v_off(32 * db + q, 4 * kb + 2 * s2 + h));
+      const int voff = HALF_V ? vh_off(32 * db + q, 2 * s2 + h) : v_off(32 * db + q, 4 * kb + 2 * s2 + h);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vbuf + voff);
       st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], st.o[db], 0, 0, 0);
     }
 }
 
-// Walk the key tiles of a unit.  SPLIT = false: all 4 waves share each tile
-// (two query tiles x two 32-row halves).  SPLIT = true: waves 0-1 take the
-// even positions of the key list and waves 2-3 the odd ones (one query tile).
-// Each step: prefetch the next K tile, S = K Q^T, barrier, store next K and
-// prefetch next V, softmax + PV, barrier, store next V.
-template <int D, bool SPLIT, int M>
-__device__ __forceinline__ void run_steps(WaveState<D>& st, u32x4 (&rs)[M],
-                                          char* smem, const int* cols, int nkeys,
-                                          const char* kbase, const char* vbase, const AttnArgs& a,
-                                          int tid, int lane, int grp) {
-  constexpr int NTHR = SPLIT ? 128 : kThreads;
-  constexpr int KN = Stage<D, NTHR>::kN;
-  static_assert(KN <= M, "staging registers");
-  constexpr int STRIDE = SPLIT ? 2 : 1;
-  constexpr int TB = Cfg<D>::kTileBytes;
-  const int t = SPLIT ? (tid & 127) : tid;
-  const int my = SPLIT ? grp : 0;
-  char* kbuf = smem + my * Cfg<D>::kSplitBytes;
-  char* vbuf = kbuf + Cfg<D>::kTileBytes;
-  const int nsteps = SPLIT ? (nkeys + 1) / 2 : nkeys;
-  const int h = lane >> 5;
-  int j = (my < nkeys) ? uni(cols[my]) : -1;
-  int jn = (STRIDE + my < nkeys) ? uni(cols[STRIDE + my]) : -1;
-  // One set of staging registers carries the next K tile during Q.K^T and
-  // then the next V tile during softmax + P.V.
-  if (j >= 0) {
-    stage_load<NTHR, KN>(rs, kbase + (int64_t)j * TB, t);
-    stage_store_k<D, NTHR, KN>(rs, kbuf, t);
-    stage_load<NTHR, KN>(rs, vbase + (int64_t)j * TB, t);
-    stage_store_v<NTHR, KN>(rs, vbuf, t);
+#define VSA_LDS __attribute__((address_space(3)))
+
+// Asynchronous global -> LDS copy (global_load_lds_dwordx4): one wave moves a
+// 1 KB block of a tile, lane L writing LDS bytes [16L, 16L + 16) of the block,
+// so each lane fetches the global chunk that the swizzle places there.
+// Completion is tracked by vmcnt; LDS reads of other buffers need no wait.
+template <int D>
+__device__ __forceinline__ void dma_k_block(char* kbuf, const char* ktile, int blk, int lane) {
+  constexpr int kCpr = Cfg<D>::kChunks;              // 16-byte chunks per K row
+  constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;     // K rows per 1 KB block
+  const int row = blk * kRpb + lane / kCpr;
+  const int sw = (D == 128) ? (row & 15) : ((row >> 1) & 7);
+  const int c = (lane % kCpr) ^ sw;
+  __builtin_amdgcn_global_load_lds(ktile + row * Cfg<D>::kRowBytes + c * 16,
+                                   (VSA_LDS void*)(kbuf + blk * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ void dma_v_block(char* vbuf, const char* vtile, int blk, int lane) {
+  const int d = blk * 8 + (lane >> 3);               // V^T rows are 128 bytes
+  const int c = (lane & 7) ^ ((d >> 1) & 7);
+  __builtin_amdgcn_global_load_lds(vtile + d * 128 + c * 16, (VSA_LDS void*)(vbuf + blk * 1024), 16,
+                                   0, 0);
+}
+
+// All blocks of one K tile and one V^T tile, spread over `nw` waves (this is
+// wave `w` of them).
+template <int D>
+__device__ __forceinline__ void dma_tile(char* buf, const char* ktile, const char* vtile, int w,
+                                         int nw, int lane) {
+  constexpr int kBlocks = Cfg<D>::kTileBytes / 1024;
+#pragma unroll
+  for (int i = 0; i < kBlocks / 4; ++i) {
+    const int blk = w * (kBlocks / 4) + i;
+    if (nw == 4 || blk < kBlocks) {
+      dma_k_block<D>(buf, ktile, blk, lane);
+      dma_v_block(buf + Cfg<D>::kTileBytes, vtile, blk, lane);
+    }
   }
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); }
+
+// One key tile of a G unit from LDS buffer CUR; the next tile is copied into
+// the other buffer by DMA while this one is computed on.
+template <int D, int CUR>
+__device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int j, int jn,
+                                       const char* kbase, const char* vbase, const AttnArgs& a,
+                                       int wave, int lane) {
+  constexpr int TB = Cfg<D>::kTileBytes;
+  const char* kbuf = smem + CUR * Cfg<D>::kSplitBytes;
+  const char* vbuf = kbuf + TB;
+  if (jn >= 0)
+    dma_tile<D>(smem + (CUR ^ 1) * Cfg<D>::kSplitBytes, kbase + (int64_t)jn * TB,
+                vbase + (int64_t)jn * TB, wave, 4, lane);
+  const TileExtent ext = tile_extent(j, a.nh, a.nw, a.T, a.H, a.W);
+  const f32x16 s0 = qk32<D>(kbuf, st, lane);
+  softmax_pv_half<D, false>(st, s0, vbuf, 0, lane, ext, a.c2);
+  const f32x16 s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
+  softmax_pv_half<D, false>(st, s1, vbuf, 1, lane, ext, a.c2);
+  wait_dma();
   lds_barrier();
-  for (int step = 0; step < nsteps; ++step) {
-    const int pnn = (step + 2) * STRIDE + my;
-    const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;  // made uniform one step later
-    if (jn >= 0) stage_load<NTHR, KN>(rs, kbase + (int64_t)jn * TB, t);
-    // The tile is consumed in two halves of 32 keys (halves the score and P
-    // registers); the K buffer is free once the second half's scores exist.
-    const uint64_t vm = (j >= 0) ? tile_valid_mask(j, a.nh, a.nw, a.T, a.H, a.W) : ~0ull;
-    const bool edge = vm != ~0ull;
-    const uint32_t bits = lane_bits(vm, h);
-    f32x16 s1;
+}
+
+// G units: all 4 waves (two query tiles x two 32-row halves) share each key
+// tile.  LDS holds two K/V buffers: while one is computed on, the next tile
+// streams into the other (a whole step to arrive, one barrier per step).
+template <int D>
+__device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const int* cols,
+                                            int nkeys, const char* kbase, const char* vbase,
+                                            const AttnArgs& a, int wave, int lane) {
+  constexpr int TB = Cfg<D>::kTileBytes;
+  int j = uni(cols[0]);
+  int jn = (1 < nkeys) ? uni(cols[1]) : -1;
+  dma_tile<D>(smem, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, wave, 4, lane);
+  wait_dma();
+  lds_barrier();
+  for (int step = 0; step < nkeys; step += 2) {
+    int jnn_v = (step + 2 < nkeys) ? cols[step + 2] : -1;
+    g_step<D, 0>(st, smem, j, jn, kbase, vbase, a, wave, lane);
+    j = jn;
+    jn = uni(jnn_v);
+    if (step + 1 >= nkeys) break;
+    jnn_v = (step + 3 < nkeys) ? cols[step + 3] : -1;
+    g_step<D, 1>(st, smem, j, jn, kbase, vbase, a, wave, lane);
+    j = jn;
+    jn = uni(jnn_v);
+  }
+}
+
+// Half-tile DMA for S units: the K rows of half kb (32 rows) and the V^T
+// columns of half kb (32 keys of each of the D rows), `nwv` waves sharing the
+// blocks (this is wave `wi` of them).
+template <int D>
+__device__ __forceinline__ void dma_half(char* buf, const char* ktile, const char* vtile, int kb,
+                                         int wi, int nwv, int lane) {
+  constexpr int kCpr = Cfg<D>::kChunks;
+  constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
+  constexpr int KH = 32 * Cfg<D>::kRowBytes;   // bytes of a K half
+  constexpr int kKBlocks = KH / 1024, kVBlocks = D * 64 / 1024;
+#pragma unroll
+  for (int i = 0; i < kKBlocks / 2; ++i) {
+    const int blk = wi * (kKBlocks / 2) + i;
+    const int row = blk * kRpb + lane / kCpr;            // row within the half
+    const int sw = (D == 128) ? (row & 15) : ((row >> 1) & 7);
+    const int c = (lane % kCpr) ^ sw;
+    __builtin_amdgcn_global_load_lds(ktile + (32 * kb + row) * Cfg<D>::kRowBytes + c * 16,
+                                     (VSA_LDS void*)(buf + blk * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kVBlocks / 2; ++i) {
+    const int blk = wi * (kVBlocks / 2) + i;
+    const int d = blk * 16 + (lane >> 2);
+    const int c4 = (lane & 3) ^ ((d >> 2) & 3);
+    __builtin_amdgcn_global_load_lds(vtile + d * 128 + (4 * kb + c4) * 16,
+                                     (VSA_LDS void*)(buf + KH + blk * 1024), 16, 0, 0);
+  }
+  (void)nwv;
+}
+
+// S units: one query tile; waves 0-1 (rows 0-31, 32-63) take the key tiles at
+// even positions of the list and waves 2-3 the odd ones.  Each key split
+// double-buffers half tiles (32 keys of K and of V^T) in its own LDS region,
+// so the two tiles a step needs fit beside their prefetches.
+template <int D>
+__device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const int* cols,
+                                            int nkeys, const char* kbase, const char* vbase,
+                                            const AttnArgs& a, int wave, int lane, int grp) {
+  constexpr int TB = Cfg<D>::kTileBytes;
+  constexpr int KH = 32 * Cfg<D>::kRowBytes;
+  constexpr int BUF = KH + D * 64;                       // one half-tile buffer
+  static_assert(4 * BUF <= Cfg<D>::kLdsBytes, "S unit buffers");
+  char* region = smem + grp * 2 * BUF;
+  const int wi = wave & 1;
+  const int nsteps = (nkeys + 1) / 2;
+  int j = (grp < nkeys) ? uni(cols[grp]) : -1;
+  int jn = (2 + grp < nkeys) ? uni(cols[2 + grp]) : -1;
+  if (j >= 0) dma_half<D>(region, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, 0, wi, 2, lane);
+  wait_dma();
+  lds_barrier();
+  for (int i = 0; i < nsteps; ++i) {
+    const int pnn = 2 * (i + 2) + grp;
+    const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;
+    TileExtent ext;
     if (j >= 0) {
-      const f32x16 s0 = qk_half<D>(kbuf, st, 0, lane);
-      softmax_pv_half<D>(st, s0, vbuf, 0, lane, edge, bits, a.c2);
-      s1 = qk_half<D>(kbuf, st, 1, lane);
+      dma_half<D>(region + BUF, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, 1, wi, 2, lane);
+      ext = tile_extent(j, a.nh, a.nw, a.T, a.H, a.W);
+      const f32x16 s0 = qk32<D>(region, st, lane);
+      softmax_pv_half<D, true>(st, s0, region + KH, 0, lane, ext, a.c2);
     }
+    wait_dma();
     lds_barrier();
-    if (jn >= 0) {
-      stage_store_k<D, NTHR, KN>(rs, kbuf, t);
-      stage_load<NTHR, KN>(rs, vbase + (int64_t)jn * TB, t);
+    if (jn >= 0)
+      dma_half<D>(region, kbase + (int64_t)jn * TB, vbase + (int64_t)jn * TB, 0, wi, 2, lane);
+    if (j >= 0) {
+      const f32x16 s1 = qk32<D>(region + BUF, st, lane);
+      softmax_pv_half<D, true>(st, s1, region + BUF + KH, 1, lane, ext, a.c2);
     }
-    if (j >= 0) softmax_pv_half<D>(st, s1, vbuf, 1, lane, edge, bits, a.c2);
+    wait_dma();
     lds_barrier();
-    if (jn >= 0) stage_store_v<NTHR, KN>(rs, vbuf, t);
     j = jn;
     jn = uni(jnn_v);
   }
@@ -574,8 +659,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   const int half = wave & 1;
   const int grp = wave >> 1;  // G: which query tile; S: which key split
   constexpr int TC = Cfg<D>::kTileChunks;
-  // staging registers shared by both unit kinds (sized for the split kind)
-  u32x4 rs[Stage<D, 128>::kN];
 
   for (;;) {
     if (tid == 0) s_unit = atomicAdd(&args.hdr_mut->counter, 1);
@@ -618,9 +701,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     const char* kbase = reinterpret_cast<const char*>(args.k) + bh * (int64_t)nT * TC * 16;
     const char* vbase = reinterpret_cast<const char*>(args.v) + bh * (int64_t)nT * TC * 16;
     if (g_mode)
-      run_steps<D, false>(st, rs, smem, cols, nkeys, kbase, vbase, args, tid, lane, grp);
+      run_steps_g<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane);
     else
-      run_steps<D, true>(st, rs, smem, cols, nkeys, kbase, vbase, args, tid, lane, grp);
+      run_steps_s<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane, grp);
 
     // S units: merge the two key splits (waves 2,3 -> waves 0,1) through LDS.
     if (!g_mode) {
@@ -653,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
 
     const bool writer = g_mode || grp == 0;
     if (writer) {
-      const float lt = st.l + __shfl_xor(st.l, 32);
+      const float lt = sum_halves(st.l);
       const int qi = 32 * half + q;  // query row within the tile
       if (u.slot < 0) {
         const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
