@@ -40,6 +40,7 @@ namespace vsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte chunk (native vector)
 
@@ -51,10 +52,11 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
 constexpr int kMinChunk = 32;          // smallest automatic key chunk (tiles)
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0), expcnt/lgkmcnt unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;
-// Automatic splitting aims at this many G units (4x the resident workgroups of
-// a 256-CU part at 2 workgroups per CU); fixed so workspace sizes do not depend
-// on the device.
-constexpr int kSplitTarget = 1024;
+// Automatic splitting of G units starts when there are fewer than this many
+// (half the resident workgroups of a 256-CU part at 2 per CU): then each is cut
+// into key chunks so that about this many exist.  Fixed so workspace sizes do
+// not depend on the device.
+constexpr int kSplitTarget = 256;
 
 struct Unit {
   int32_t row[2];  // CSR rows (global); S units use row[0] only
@@ -69,15 +71,61 @@ struct Comb {
   int32_t row, slot0, stride, n;
 };
 
+// Units are dealt to 8 queues in chunks of kQueueChunk consecutive units
+// (queue x owns units u with (u / kQueueChunk) % 8 == x).  Workgroup b serves
+// queue b % 8 first, the XCD that the hardware dispatches it to, so
+// neighbouring query tiles (overlapping key windows, the same head's K/V)
+// share that XCD's L2; an empty queue sends its workgroups to the others.
+constexpr int kQueues = 8;
+constexpr int kQueueChunk = 16;
+
 struct Header {
   int32_t n_units;
   int32_t counter;
   int32_t n_comb;
   int32_t chunks_g;
   int32_t overflow;
-  int32_t pad[59];
+  int32_t pad0[3];
+  int32_t queue[kQueues];
+  int32_t pad[48];
 };
 static_assert(sizeof(Header) == 256, "header layout");
+
+// Extent of a key tile inside the grid (tokens valid along t, h, w); a tile
+// with any extent below 4 holds padding slots that must not be attended.
+struct TileExtent {
+  int vt, vh, vw;
+  bool edge;
+};
+
+// Packed extent of a tile: vt | vh << 4 | vw << 8 | edge << 12 (written once per
+// call by the plan kernel, read per key tile by the attention kernel).
+__device__ __forceinline__ int pack_extent(int tau, int nh, int nw, int T, int H, int W) {
+  const int tw = tau % nw, th = (tau / nw) % nh, tt = tau / (nw * nh);
+  const int vt = min(kTile, T - tt * kTile), vh = min(kTile, H - th * kTile),
+            vw = min(kTile, W - tw * kTile);
+  const int edge = (vt < kTile) | (vh < kTile) | (vw < kTile);
+  return vt | (vh << 4) | (vw << 8) | (edge << 12);
+}
+
+__device__ __forceinline__ TileExtent unpack_extent(int code) {
+  TileExtent e;
+  e.vt = code & 15;
+  e.vh = (code >> 4) & 15;
+  e.vw = (code >> 8) & 15;
+  e.edge = (code >> 12) & 1;
+  return e;
+}
+
+__device__ __forceinline__ TileExtent tile_extent(int tau, int nh, int nw, int T, int H, int W) {
+  TileExtent e;
+  const int tw = tau % nw, th = (tau / nw) % nh, tt = tau / (nw * nh);
+  e.vt = min(kTile, T - tt * kTile);
+  e.vh = min(kTile, H - th * kTile);
+  e.vw = min(kTile, W - tw * kTile);
+  e.edge = (e.vt < kTile) | (e.vh < kTile) | (e.vw < kTile);
+  return e;
+}
 
 }  // namespace
 
@@ -113,6 +161,7 @@ AttnLayout attn_layout(const vsa_shape& s, int kv_chunk) {
   L.off_comb = take(sizeof(Comb) * (L.rows + 1));
   L.off_po = take((size_t)L.max_slots * kTileTokens * s.head_dim * 4);
   L.off_pml = take((size_t)L.max_slots * kTileTokens * 2 * 4);
+  L.off_ext = take(4 * (size_t)g.nT);
   L.total = o;
   return L;
 }
@@ -124,9 +173,10 @@ namespace {
 struct PlanArgs {
   const int* row_ptr;
   int bh, nT, kv_chunk, target;
+  int nh, nw, T, H, W;
   int64_t max_units, max_slots;
   Header* hdr;
-  int *E, *gbase, *grows, *sinfo, *su, *sp, *sc;
+  int *E, *gbase, *grows, *sinfo, *su, *sp, *sc, *ext;
   Unit* units;
   Comb* comb;
 };
@@ -156,6 +206,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   const int64_t seg = (rows + kPlanThreads - 1) / kPlanThreads;
   const int64_t r0 = min(rows, seg * threadIdx.x), r1 = min(rows, r0 + seg);
   auto len_of = [&](int64_t r) { return p.row_ptr[r + 1] - p.row_ptr[r]; };
+
+  for (int tau = threadIdx.x; tau < nT; tau += kPlanThreads)
+    p.ext[tau] = pack_extent(tau, p.nh, p.nw, p.T, p.H, p.W);
 
   // A: E[r] = number of complete rows (every key tile) before row r.
   int cnt = 0;
@@ -249,6 +302,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       p.hdr->n_comb = 0;
       p.hdr->overflow = 1;
       p.hdr->counter = 0;
+      for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = 0;
     }
     return;
   }
@@ -310,6 +364,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     p.hdr->chunks_g = sg;
     p.hdr->overflow = 0;
     p.hdr->counter = 0;
+    for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = 0;
   }
 }
 
@@ -323,6 +378,7 @@ struct AttnArgs {
   const int* col_idx;
   uint16_t* o;         // [BH][nT*64][D]
   float* lse;          // [BH][nT*64] or null
+  const int* ext;      // packed extent per key tile
   const Header* hdr;
   Header* hdr_mut;
   const Unit* units;
@@ -400,23 +456,6 @@ __device__ __forceinline__ f32x16 qk32(const char* k32, const WaveState<D>& st, 
 // bank groups).
 __device__ __forceinline__ int vh_off(int d, int c4) { return d * 64 + ((c4 ^ ((d >> 2) & 3)) << 4); }
 
-// Extent of a key tile inside the grid (tokens valid along t, h, w); a tile
-// with any extent below 4 holds padding slots that must not be attended.
-struct TileExtent {
-  int vt, vh, vw;
-  bool edge;
-};
-
-__device__ __forceinline__ TileExtent tile_extent(int tau, int nh, int nw, int T, int H, int W) {
-  TileExtent e;
-  const int tw = tau % nw, th = (tau / nw) % nh, tt = tau / (nw * nh);
-  e.vt = min(kTile, T - tt * kTile);
-  e.vh = min(kTile, H - th * kTile);
-  e.vw = min(kTile, W - tw * kTile);
-  e.edge = (e.vt < kTile) | (e.vh < kTile) | (e.vw < kTile);
-  return e;
-}
-
 // Values of lane l and lane l ^ 32 combined (v_permlane32_swap exchanges the
 // two 32-lane halves; with the same register on both sides, the pair of
 // results holds both halves' values in every lane).
@@ -466,14 +505,19 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
   // every tile holds at least one valid key, so the running max is finite here
   const float mneg = -st.m;
   bf16x8 pb[2];
-  float lsum = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c2, mneg));
-    lsum += pv;
-    pb[r >> 3][r & 7] = (__bf16)pv;
+  for (int r = 0; r < 16; ++r)
+    pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], c2, mneg));
+  // Row sum of the bf16 probabilities that P.V multiplies (one v_dot2 per pair:
+  // numerator and denominator use the same rounded weights).
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float lsum = st.l;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const bf16x2 pair = {pb[r >> 3][r & 7], pb[r >> 3][(r & 7) + 1]};
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
   }
-  st.l += lsum;
+  st.l = lsum;
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -490,46 +534,54 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
 // 1 KB block of a tile, lane L writing LDS bytes [16L, 16L + 16) of the block,
 // so each lane fetches the global chunk that the swizzle places there.
 // Completion is tracked by vmcnt; LDS reads of other buffers need no wait.
+// Addresses are a wave-uniform base plus a 32-bit per-lane offset, so the
+// loads use the scalar-base form and the per-lane parts are a few registers.
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t lane_off, char* lds_block) {
+  __builtin_amdgcn_global_load_lds(gbase + lane_off, (VSA_LDS void*)lds_block, 16, 0, 0);
+}
+
+// Per-lane byte offset, within a K block of rows [r0, r0 + rows-per-block),
+// of the global chunk that lands at LDS position 16*lane; only r0 mod 16
+// matters for the swizzle.
 template <int D>
-__device__ __forceinline__ void dma_k_block(char* kbuf, const char* ktile, int blk, int lane) {
-  constexpr int kCpr = Cfg<D>::kChunks;              // 16-byte chunks per K row
-  constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;     // K rows per 1 KB block
-  const int row = blk * kRpb + lane / kCpr;
+__device__ __forceinline__ uint32_t k_lane_off(int r0, int lane) {
+  constexpr int kCpr = Cfg<D>::kChunks;
+  const int row = r0 + lane / kCpr;
   const int sw = (D == 128) ? (row & 15) : ((row >> 1) & 7);
-  const int c = (lane % kCpr) ^ sw;
-  __builtin_amdgcn_global_load_lds(ktile + row * Cfg<D>::kRowBytes + c * 16,
-                                   (VSA_LDS void*)(kbuf + blk * 1024), 16, 0, 0);
+  return (uint32_t)((lane / kCpr) * Cfg<D>::kRowBytes + (((lane % kCpr) ^ sw) << 4));
 }
 
-__device__ __forceinline__ void dma_v_block(char* vbuf, const char* vtile, int blk, int lane) {
-  const int d = blk * 8 + (lane >> 3);               // V^T rows are 128 bytes
-  const int c = (lane & 7) ^ ((d >> 1) & 7);
-  __builtin_amdgcn_global_load_lds(vtile + d * 128 + c * 16, (VSA_LDS void*)(vbuf + blk * 1024), 16,
-                                   0, 0);
+// Same for a V^T block of 8 rows of 128 bytes starting at row d0.
+__device__ __forceinline__ uint32_t v_lane_off(int d0, int lane) {
+  const int d = d0 + (lane >> 3);
+  return (uint32_t)((lane >> 3) * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4));
 }
 
-// All blocks of one K tile and one V^T tile, spread over `nw` waves (this is
-// wave `w` of them).
+// All blocks of one K tile and one V^T tile, spread over the 4 waves of the
+// workgroup (this is wave `w`).
 template <int D>
 __device__ __forceinline__ void dma_tile(char* buf, const char* ktile, const char* vtile, int w,
                                          int nw, int lane) {
   constexpr int kBlocks = Cfg<D>::kTileBytes / 1024;
+  constexpr int kPer = kBlocks / 4;
+  constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
+  (void)nw;
 #pragma unroll
-  for (int i = 0; i < kBlocks / 4; ++i) {
-    const int blk = w * (kBlocks / 4) + i;
-    if (nw == 4 || blk < kBlocks) {
-      dma_k_block<D>(buf, ktile, blk, lane);
-      dma_v_block(buf + Cfg<D>::kTileBytes, vtile, blk, lane);
-    }
+  for (int i = 0; i < kPer; ++i) {
+    const int blk = w * kPer + i;  // rows blk*kRpb.. (K) / blk*8.. (V); the swizzle
+                                   // phase depends on i only (w*kPer*kRpb % 16 == 0)
+    dma16(ktile + blk * 1024, k_lane_off<D>(i * kRpb, lane), buf + blk * 1024);
+    dma16(vtile + blk * 1024, v_lane_off(i * 8, lane), buf + Cfg<D>::kTileBytes + blk * 1024);
   }
 }
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); }
 
 // One key tile of a G unit from LDS buffer CUR; the next tile is copied into
-// the other buffer by DMA while this one is computed on.
+// the other buffer by DMA while this one is computed on.  Both halves' score
+// MFMAs are issued before the first softmax so they run under its VALU work.
 template <int D, int CUR>
-__device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int j, int jn,
+__device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int code,
                                        const char* kbase, const char* vbase, const AttnArgs& a,
                                        int wave, int lane) {
   constexpr int TB = Cfg<D>::kTileBytes;
@@ -538,10 +590,10 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int j, int 
   if (jn >= 0)
     dma_tile<D>(smem + (CUR ^ 1) * Cfg<D>::kSplitBytes, kbase + (int64_t)jn * TB,
                 vbase + (int64_t)jn * TB, wave, 4, lane);
-  const TileExtent ext = tile_extent(j, a.nh, a.nw, a.T, a.H, a.W);
+  const TileExtent ext = unpack_extent(code);
   const f32x16 s0 = qk32<D>(kbuf, st, lane);
-  softmax_pv_half<D, false>(st, s0, vbuf, 0, lane, ext, a.c2);
   const f32x16 s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
+  softmax_pv_half<D, false>(st, s0, vbuf, 0, lane, ext, a.c2);
   softmax_pv_half<D, false>(st, s1, vbuf, 1, lane, ext, a.c2);
   wait_dma();
   lds_barrier();
@@ -550,57 +602,60 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int j, int 
 // G units: all 4 waves (two query tiles x two 32-row halves) share each key
 // tile.  LDS holds two K/V buffers: while one is computed on, the next tile
 // streams into the other (a whole step to arrive, one barrier per step).
+// Column indices are read two tiles ahead and the next tile's extent one
+// tile ahead, so neither load is waited on.
 template <int D>
 __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const int* cols,
                                             int nkeys, const char* kbase, const char* vbase,
                                             const AttnArgs& a, int wave, int lane) {
   constexpr int TB = Cfg<D>::kTileBytes;
-  int j = uni(cols[0]);
+  const int j0 = uni(cols[0]);
   int jn = (1 < nkeys) ? uni(cols[1]) : -1;
-  dma_tile<D>(smem, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, wave, 4, lane);
+  int code = uni(a.ext[j0]);
+  dma_tile<D>(smem, kbase + (int64_t)j0 * TB, vbase + (int64_t)j0 * TB, wave, 4, lane);
   wait_dma();
   lds_barrier();
   for (int step = 0; step < nkeys; step += 2) {
     int jnn_v = (step + 2 < nkeys) ? cols[step + 2] : -1;
-    g_step<D, 0>(st, smem, j, jn, kbase, vbase, a, wave, lane);
-    j = jn;
+    int cn_v = (jn >= 0) ? a.ext[jn] : 0;
+    g_step<D, 0>(st, smem, jn, code, kbase, vbase, a, wave, lane);
+    code = uni(cn_v);
     jn = uni(jnn_v);
     if (step + 1 >= nkeys) break;
     jnn_v = (step + 3 < nkeys) ? cols[step + 3] : -1;
-    g_step<D, 1>(st, smem, j, jn, kbase, vbase, a, wave, lane);
-    j = jn;
+    cn_v = (jn >= 0) ? a.ext[jn] : 0;
+    g_step<D, 1>(st, smem, jn, code, kbase, vbase, a, wave, lane);
+    code = uni(cn_v);
     jn = uni(jnn_v);
   }
 }
 
 // Half-tile DMA for S units: the K rows of half kb (32 rows) and the V^T
-// columns of half kb (32 keys of each of the D rows), `nwv` waves sharing the
-// blocks (this is wave `wi` of them).
+// columns of half kb (32 keys of each of the D rows), the two waves of a key
+// split sharing the blocks (this is wave `wi` of them).
 template <int D>
 __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const char* vtile, int kb,
                                          int wi, int nwv, int lane) {
-  constexpr int kCpr = Cfg<D>::kChunks;
   constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
   constexpr int KH = 32 * Cfg<D>::kRowBytes;   // bytes of a K half
   constexpr int kKBlocks = KH / 1024, kVBlocks = D * 64 / 1024;
+  (void)nwv;
 #pragma unroll
   for (int i = 0; i < kKBlocks / 2; ++i) {
-    const int blk = wi * (kKBlocks / 2) + i;
-    const int row = blk * kRpb + lane / kCpr;            // row within the half
-    const int sw = (D == 128) ? (row & 15) : ((row >> 1) & 7);
-    const int c = (lane % kCpr) ^ sw;
-    __builtin_amdgcn_global_load_lds(ktile + (32 * kb + row) * Cfg<D>::kRowBytes + c * 16,
-                                     (VSA_LDS void*)(buf + blk * 1024), 16, 0, 0);
+    const int blk = wi * (kKBlocks / 2) + i;   // swizzle phase depends on i only
+    dma16(ktile + (32 * kb) * Cfg<D>::kRowBytes + blk * 1024, k_lane_off<D>(i * kRpb, lane),
+          buf + blk * 1024);
   }
 #pragma unroll
   for (int i = 0; i < kVBlocks / 2; ++i) {
     const int blk = wi * (kVBlocks / 2) + i;
+    // rows d = blk*16 + lane/4 (64-byte rows of 32 keys); chunk 4kb + c4 of the
+    // global 128-byte row
     const int d = blk * 16 + (lane >> 2);
     const int c4 = (lane & 3) ^ ((d >> 2) & 3);
-    __builtin_amdgcn_global_load_lds(vtile + d * 128 + (4 * kb + c4) * 16,
-                                     (VSA_LDS void*)(buf + KH + blk * 1024), 16, 0, 0);
+    const uint32_t off = (uint32_t)((lane >> 2) * 128 + (c4 << 4));
+    dma16(vtile + blk * 16 * 128 + kb * 64, off, buf + KH + blk * 1024);
   }
-  (void)nwv;
 }
 
 // S units: one query tile; waves 0-1 (rows 0-31, 32-63) take the key tiles at
@@ -620,16 +675,17 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
   const int nsteps = (nkeys + 1) / 2;
   int j = (grp < nkeys) ? uni(cols[grp]) : -1;
   int jn = (2 + grp < nkeys) ? uni(cols[2 + grp]) : -1;
+  int code = (j >= 0) ? uni(a.ext[j]) : 0;
   if (j >= 0) dma_half<D>(region, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, 0, wi, 2, lane);
   wait_dma();
   lds_barrier();
   for (int i = 0; i < nsteps; ++i) {
     const int pnn = 2 * (i + 2) + grp;
     const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;
-    TileExtent ext;
+    const int cn_v = (jn >= 0) ? a.ext[jn] : 0;
+    const TileExtent ext = unpack_extent(code);
     if (j >= 0) {
       dma_half<D>(region + BUF, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, 1, wi, 2, lane);
-      ext = tile_extent(j, a.nh, a.nw, a.T, a.H, a.W);
       const f32x16 s0 = qk32<D>(region, st, lane);
       softmax_pv_half<D, true>(st, s0, region + KH, 0, lane, ext, a.c2);
     }
@@ -644,6 +700,7 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     wait_dma();
     lds_barrier();
     j = jn;
+    code = uni(cn_v);
     jn = uni(jnn_v);
   }
 }
@@ -658,14 +715,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   const int n_units = args.hdr->n_units;
   const int half = wave & 1;
   const int grp = wave >> 1;  // G: which query tile; S: which key split
+  const int home = blockIdx.x % kQueues;
   constexpr int TC = Cfg<D>::kTileChunks;
 
   for (;;) {
-    if (tid == 0) s_unit = atomicAdd(&args.hdr_mut->counter, 1);
+    if (tid == 0) {
+      int u = -1;
+      for (int k = 0; k < kQueues; ++k) {
+        const int x = (home + k) % kQueues;
+        const int idx = atomicAdd(&args.hdr_mut->queue[x], 1);
+        const int cand = (idx / kQueueChunk) * (kQueues * kQueueChunk) + x * kQueueChunk +
+                         idx % kQueueChunk;
+        if (cand < n_units) {
+          u = cand;
+          break;
+        }
+      }
+      s_unit = u;
+    }
     lds_barrier();
     const int ui = uni(s_unit);
     lds_barrier();
-    if (ui >= n_units) break;
+    if (ui < 0) break;
     Unit u = args.units[ui];
     u.row[0] = uni(u.row[0]);
     u.row[1] = uni(u.row[1]);
@@ -836,6 +907,12 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   pa.su = reinterpret_cast<int*>(w + L.off_su);
   pa.sp = reinterpret_cast<int*>(w + L.off_sp);
   pa.sc = reinterpret_cast<int*>(w + L.off_sc);
+  pa.ext = reinterpret_cast<int*>(w + L.off_ext);
+  pa.nh = g.nh;
+  pa.nw = g.nw;
+  pa.T = s.T;
+  pa.H = s.H;
+  pa.W = s.W;
   pa.units = reinterpret_cast<Unit*>(w + L.off_units);
   pa.comb = reinterpret_cast<Comb*>(w + L.off_comb);
   plan_kernel<<<1, kPlanThreads, 0, stream>>>(pa);
@@ -848,6 +925,7 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   aa.col_idx = col_idx;
   aa.o = static_cast<uint16_t*>(o);
   aa.lse = lse;
+  aa.ext = pa.ext;
   aa.hdr = hdr;
   aa.hdr_mut = hdr;
   aa.units = pa.units;
