@@ -46,6 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte chunk (n
 
 constexpr int kThreads = 256;
 constexpr int kPlanThreads = 1024;
+constexpr int kLenBuckets = 1024;      // key-count buckets of the unit order
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
@@ -154,7 +155,6 @@ AttnLayout attn_layout(const vsa_shape& s, int kv_chunk) {
   L.off_gbase = take(4 * (L.bh + 1));
   L.off_grows = take(4 * (L.rows + 2));
   L.off_sinfo = take(4 * (L.rows + 1));
-  L.off_su = take(4 * (L.rows + 1));
   L.off_sp = take(4 * (L.rows + 1));
   L.off_sc = take(4 * (L.rows + 1));
   L.off_units = take(sizeof(Unit) * L.max_units);
@@ -176,7 +176,7 @@ struct PlanArgs {
   int nh, nw, T, H, W;
   int64_t max_units, max_slots;
   Header* hdr;
-  int *E, *gbase, *grows, *sinfo, *su, *sp, *sc, *ext;
+  int *E, *gbase, *grows, *sinfo, *sp, *sc, *ext;
   Unit* units;
   Comb* comb;
 };
@@ -278,15 +278,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     c_sc += (n > 1);
   }
   int nSU, nSP, nSC;
-  int bu = block_exclusive_scan(c_su, buf, &nSU);
+  (void)block_exclusive_scan(c_su, buf, &nSU);
   int bp = block_exclusive_scan(c_sp, buf, &nSP);
   int bc = block_exclusive_scan(c_sc, buf, &nSC);
   for (int64_t r = r0; r < r1; ++r) {
     const int n = p.sinfo[r];
-    p.su[r] = bu;
     p.sp[r] = bp;
     p.sc[r] = bc;
-    bu += n;
     bp += (n > 1) ? n : 0;
     bc += (n > 1);
   }
@@ -307,7 +305,45 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     return;
   }
 
-  // D: emit units (G first: the longest) and combine entries.
+  // D: unit order, longest first, so that no long unit starts late.  S units
+  // of at least half a full row (complete rows left over from the pairing)
+  // come first, then the G units (all of one length), then the other S units
+  // by descending key count (counting sort over kLenBuckets buckets; order
+  // within a bucket is arbitrary and does not affect any result).
+  __shared__ int hist[kLenBuckets];
+  __shared__ int s_front;
+  static_assert(kLenBuckets == kPlanThreads, "one bucket per plan thread");
+  hist[threadIdx.x] = 0;
+  if (threadIdx.x == 0) s_front = 0;
+  __syncthreads();
+  auto s_unit_len = [&](int len, int n, int c) {
+    const int ch = (n > 1) ? chunk_s : max(len, 0);
+    return max(0, min(len, (c + 1) * ch) - c * ch);
+  };
+  auto is_front = [&](int lu) { return 2 * lu >= nT && nT > 0; };
+  for (int64_t r = r0; r < r1; ++r) {
+    const int n = p.sinfo[r];
+    const int len = len_of(r);
+    for (int c = 0; c < n; ++c) {
+      const int lu = s_unit_len(len, n, c);
+      if (is_front(lu))
+        atomicAdd(&s_front, 1);
+      else
+        atomicAdd(&hist[min(lu, kLenBuckets - 1)], 1);
+    }
+  }
+  __syncthreads();
+  const int bucket = kLenBuckets - 1 - threadIdx.x;  // descending lengths
+  int n_rest;
+  const int bstart = block_exclusive_scan(hist[bucket], buf, &n_rest);
+  const int n_front = s_front;
+  __syncthreads();
+  hist[bucket] = bstart;  // becomes the bucket's next free position
+  if (threadIdx.x == 0) s_front = 0;
+  __syncthreads();
+  const int64_t rest_base = (int64_t)n_front + nGU;
+
+  // emit units and combine entries
   for (int64_t i = threadIdx.x; i < nGU; i += kPlanThreads) {
     const int gi = (int)(i / sg), c = (int)(i % sg);
     Unit u;
@@ -318,7 +354,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     u.slot = (sg > 1) ? (int)(2 * i) : -1;
     u.mode = 0;
     u.pad[0] = u.pad[1] = 0;
-    p.units[i] = u;
+    p.units[n_front + i] = u;
   }
   if (sg > 1) {
     for (int64_t i = threadIdx.x; i < 2LL * NG; i += kPlanThreads) {
@@ -342,12 +378,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       u.row[0] = (int)r;
       u.row[1] = -1;
       u.kb = c * ch;
-      u.ke = min(len, u.kb + ch);
-      if (u.ke < u.kb) u.ke = u.kb;
+      u.ke = u.kb + s_unit_len(len, n, c);
       u.slot = (n > 1) ? (int)(gslots + p.sp[r] + c) : -1;
       u.mode = 1;
       u.pad[0] = u.pad[1] = 0;
-      p.units[nGU + p.su[r] + c] = u;
+      const int lu = u.ke - u.kb;
+      const int64_t pos = is_front(lu) ? (int64_t)atomicAdd(&s_front, 1)
+                                       : rest_base + atomicAdd(&hist[min(lu, kLenBuckets - 1)], 1);
+      p.units[pos] = u;
     }
     if (n > 1) {
       Comb cb;
@@ -904,7 +942,6 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   pa.gbase = reinterpret_cast<int*>(w + L.off_gbase);
   pa.grows = reinterpret_cast<int*>(w + L.off_grows);
   pa.sinfo = reinterpret_cast<int*>(w + L.off_sinfo);
-  pa.su = reinterpret_cast<int*>(w + L.off_su);
   pa.sp = reinterpret_cast<int*>(w + L.off_sp);
   pa.sc = reinterpret_cast<int*>(w + L.off_sc);
   pa.ext = reinterpret_cast<int*>(w + L.off_ext);
