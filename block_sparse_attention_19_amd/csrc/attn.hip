@@ -46,7 +46,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte chunk (n
 
 constexpr int kThreads = 256;
 constexpr int kPlanThreads = 1024;
-constexpr int kLenBuckets = 1024;      // key-count buckets of the unit order
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
@@ -305,42 +304,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     return;
   }
 
-  // D: unit order, longest first, so that no long unit starts late.  S units
-  // of at least half a full row (complete rows left over from the pairing)
-  // come first, then the G units (all of one length), then the other S units
-  // by descending key count (counting sort over kLenBuckets buckets; order
-  // within a bucket is arbitrary and does not affect any result).
-  __shared__ int hist[kLenBuckets];
+  // D: unit order.  S units of at least half a full row (complete rows left
+  // over from the pairing) come first, so that no unit as long as a G unit
+  // starts late; then the G units; then the other S units in row order, so
+  // that neighbouring query tiles, whose key windows overlap, run close in
+  // time on one XCD and share its L2.
   __shared__ int s_front;
-  static_assert(kLenBuckets == kPlanThreads, "one bucket per plan thread");
-  hist[threadIdx.x] = 0;
   if (threadIdx.x == 0) s_front = 0;
-  __syncthreads();
   auto s_unit_len = [&](int len, int n, int c) {
     const int ch = (n > 1) ? chunk_s : max(len, 0);
     return max(0, min(len, (c + 1) * ch) - c * ch);
   };
   auto is_front = [&](int lu) { return 2 * lu >= nT && nT > 0; };
+  int c_rest = 0, c_front = 0;
   for (int64_t r = r0; r < r1; ++r) {
     const int n = p.sinfo[r];
     const int len = len_of(r);
     for (int c = 0; c < n; ++c) {
-      const int lu = s_unit_len(len, n, c);
-      if (is_front(lu))
-        atomicAdd(&s_front, 1);
+      if (is_front(s_unit_len(len, n, c)))
+        ++c_front;
       else
-        atomicAdd(&hist[min(lu, kLenBuckets - 1)], 1);
+        ++c_rest;
     }
   }
-  __syncthreads();
-  const int bucket = kLenBuckets - 1 - threadIdx.x;  // descending lengths
-  int n_rest;
-  const int bstart = block_exclusive_scan(hist[bucket], buf, &n_rest);
-  const int n_front = s_front;
-  __syncthreads();
-  hist[bucket] = bstart;  // becomes the bucket's next free position
-  if (threadIdx.x == 0) s_front = 0;
-  __syncthreads();
+  int n_rest, n_front;
+  int rest_pos = block_exclusive_scan(c_rest, buf, &n_rest);
+  (void)block_exclusive_scan(c_front, buf, &n_front);
   const int64_t rest_base = (int64_t)n_front + nGU;
 
   // emit units and combine entries
@@ -382,9 +371,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       u.slot = (n > 1) ? (int)(gslots + p.sp[r] + c) : -1;
       u.mode = 1;
       u.pad[0] = u.pad[1] = 0;
-      const int lu = u.ke - u.kb;
-      const int64_t pos = is_front(lu) ? (int64_t)atomicAdd(&s_front, 1)
-                                       : rest_base + atomicAdd(&hist[min(lu, kLenBuckets - 1)], 1);
+      const int64_t pos = is_front(u.ke - u.kb) ? (int64_t)atomicAdd(&s_front, 1)
+                                                : rest_base + rest_pos++;
       p.units[pos] = u;
     }
     if (n > 1) {
