@@ -150,12 +150,9 @@ AttnLayout attn_layout(const vsa_shape& s, int kv_chunk) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
   take(sizeof(Header));
-  L.off_E = take(4 * (L.rows + 1));
+  L.off_cbase = take(4 * (L.bh + 1));
   L.off_gbase = take(4 * (L.bh + 1));
   L.off_grows = take(4 * (L.rows + 2));
-  L.off_sinfo = take(4 * (L.rows + 1));
-  L.off_sp = take(4 * (L.rows + 1));
-  L.off_sc = take(4 * (L.rows + 1));
   L.off_units = take(sizeof(Unit) * L.max_units);
   L.off_comb = take(sizeof(Comb) * (L.rows + 1));
   L.off_po = take((size_t)L.max_slots * kTileTokens * s.head_dim * 4);
@@ -175,67 +172,163 @@ struct PlanArgs {
   int nh, nw, T, H, W;
   int64_t max_units, max_slots;
   Header* hdr;
-  int *E, *gbase, *grows, *sinfo, *sp, *sc, *ext;
+  int *cbase, *gbase, *grows, *ext;
   Unit* units;
   Comb* comb;
 };
 
-// Exclusive scan of one int per thread over the 1024-thread block; returns the
-// thread's prefix and writes the total to *total.
-__device__ int block_exclusive_scan(int v, int* buf, int* total) {
-  buf[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int add = (threadIdx.x >= off) ? buf[threadIdx.x - off] : 0;
-    __syncthreads();
-    buf[threadIdx.x] += add;
-    __syncthreads();
+// Exclusive scan of one int per thread over the 1024-thread block (wave scans
+// by lane shuffles, then a scan of the 16 wave sums); returns the thread's
+// prefix and the block total.  `ws` is 16 ints of LDS.
+__device__ int block_exclusive_scan(int v, int* ws, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  const int incl = buf[threadIdx.x];
-  *total = buf[kPlanThreads - 1];
+  if (lane == 63) ws[w] = x;
   __syncthreads();
-  return incl - v;
+  if (w == 0) {
+    int s = (lane < kPlanThreads / 64) ? ws[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < kPlanThreads / 64; d <<= 1) {
+      const int y = __shfl_up(s, d);
+      if (lane >= d) s += y;
+    }
+    if (lane < kPlanThreads / 64) ws[lane] = s;
+  }
+  __syncthreads();
+  const int before = (w > 0) ? ws[w - 1] : 0;
+  *total = ws[kPlanThreads / 64 - 1];
+  __syncthreads();
+  return before + x - v;
 }
 
+// Rows are taken in blocks of kPlanSeg * kPlanThreads; thread t holds the
+// kPlanSeg consecutive rows starting at kPlanSeg * t of the block in registers.
+// Row indices fit in 32 bits (rows * 64 tokens is checked against INT_MAX on
+// the host), so all index arithmetic here is 32-bit, and the (batch, head) of
+// a row is tracked incrementally instead of divided out.
+constexpr int kPlanSeg = 8;
+constexpr int kPlanBlock = kPlanSeg * kPlanThreads;
+
+__device__ __forceinline__ void load_lengths(const int* row_ptr, int rows, int r0,
+                                             int (&len)[kPlanSeg]) {
+  int ptr[kPlanSeg + 1];
+#pragma unroll
+  for (int j = 0; j <= kPlanSeg; ++j) ptr[j] = row_ptr[min(rows, r0 + j)];
+#pragma unroll
+  for (int j = 0; j < kPlanSeg; ++j) len[j] = (r0 + j < rows) ? ptr[j + 1] - ptr[j] : -1;
+}
+
+// Work plan of one call: G units (pairs of complete rows of one (batch, head),
+// optionally cut into key chunks), S units (every other row, cut into chunks of
+// kv_chunk keys when that is set), their order, partial-output slots and
+// combine entries.  Pass 1 scans the complete rows (their count before each
+// (batch, head)) and totals the S units of the other rows; the per-(batch,
+// head) scan then fixes the pairing, the G chunking and every total; pass 2
+// places each row.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
-  __shared__ int buf[kPlanThreads];
-  __shared__ int s_chunk_g, s_sg;
-  const int nT = p.nT;
-  const int64_t rows = (int64_t)p.bh * nT;
-  const int64_t seg = (rows + kPlanThreads - 1) / kPlanThreads;
-  const int64_t r0 = min(rows, seg * threadIdx.x), r1 = min(rows, r0 + seg);
-  auto len_of = [&](int64_t r) { return p.row_ptr[r + 1] - p.row_ptr[r]; };
+  __shared__ int ws[kPlanThreads / 64];
+  __shared__ int s_chunk_g, s_sg, s_front;
+  const int nT = p.nT;  // >= 1
+  const int t = threadIdx.x;
+  const int rows = p.bh * nT;
+  const bool chunked = p.kv_chunk > 0;
+  const int chunk_s = p.kv_chunk;
+  // S chunks of a row of `len` keys, and the key count of chunk c
+  auto n_chunks = [&](int len) { return (!chunked || len <= 0) ? 1 : (len + chunk_s - 1) / chunk_s; };
+  auto chunk_len = [&](int len, int n, int c) {
+    if (n == 1) return max(len, 0);
+    return max(0, min(len, (c + 1) * chunk_s) - c * chunk_s);
+  };
+  // S units of at least half a full row go first (see the unit order below)
+  auto is_front = [&](int lu) { return 2 * lu >= nT; };
+  auto n_front_of = [&](int len, int n) {
+    if (n == 1) return (int)is_front(max(len, 0));
+    int f = 0;
+    for (int c = 0; c < n; ++c) f += is_front(chunk_len(len, n, c));
+    return f;
+  };
 
-  for (int tau = threadIdx.x; tau < nT; tau += kPlanThreads)
-    p.ext[tau] = pack_extent(tau, p.nh, p.nw, p.T, p.H, p.W);
+  for (int tau = t; tau < nT; tau += kPlanThreads) p.ext[tau] = pack_extent(tau, p.nh, p.nw, p.T, p.H, p.W);
+  if (t == 0) s_front = 0;
 
-  // A: E[r] = number of complete rows (every key tile) before row r.
-  int cnt = 0;
-  for (int64_t r = r0; r < r1; ++r) cnt += (len_of(r) == nT);
-  int tot;
-  int base = block_exclusive_scan(cnt, buf, &tot);
-  for (int64_t r = r0; r < r1; ++r) {
-    p.E[r] = base;
-    base += (len_of(r) == nT);
+  // pass 1: cbase[b] = complete rows before (b, h) (a scan of the complete-row
+  // flags in row order), and the S totals of the incomplete rows
+  int a_units = 0, a_front = 0, a_slots = 0, a_comb = 0;
+  int carry_c = 0;
+  for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
+    const int r0 = c0 + kPlanSeg * t;
+    int len[kPlanSeg];
+    load_lengths(p.row_ptr, rows, r0, len);
+    int n_c = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanSeg; ++j) n_c += (len[j] == nT);
+    int blk_c;
+    int e = carry_c + block_exclusive_scan(n_c, ws, &blk_c);
+    int b = min(r0, rows) / nT, pos = min(r0, rows) - b * nT;  // (b, h) of row r0 + j, offset in it
+#pragma unroll
+    for (int j = 0; j < kPlanSeg; ++j) {
+      if (len[j] >= 0) {
+        if (pos == 0) p.cbase[b] = e;
+        if (len[j] == nT) {
+          ++e;
+        } else {
+          const int n = n_chunks(len[j]);
+          a_units += n;
+          a_front += n_front_of(len[j], n);
+          if (n > 1) {
+            a_slots += n;
+            a_comb += 1;
+          }
+        }
+      }
+      if (++pos == nT) {
+        pos = 0;
+        ++b;
+      }
+    }
+    carry_c += blk_c;
   }
-  if (threadIdx.x == 0) p.E[rows] = tot;
+  if (t == 0) p.cbase[p.bh] = carry_c;
   __syncthreads();
 
-  // A2: pairs of complete rows per (b, h) -> G groups; gbase = exclusive scan.
-  const int64_t segb = (p.bh + kPlanThreads - 1) / kPlanThreads;
-  const int64_t b0 = min((int64_t)p.bh, segb * threadIdx.x), b1 = min((int64_t)p.bh, b0 + segb);
-  int gcnt = 0;
-  for (int64_t b = b0; b < b1; ++b) gcnt += (p.E[(b + 1) * nT] - p.E[b * nT]) / 2;
-  int NG;
-  int gb = block_exclusive_scan(gcnt, buf, &NG);
-  for (int64_t b = b0; b < b1; ++b) {
-    p.gbase[b] = gb;
-    gb += (p.E[(b + 1) * nT] - p.E[b * nT]) / 2;
+  // per (b, h): pairs of complete rows -> G groups (gbase = their exclusive
+  // scan); a complete row left over from the pairing becomes an S unit
+  const int segb = (p.bh + kPlanThreads - 1) / kPlanThreads;
+  const int b0 = min(p.bh, segb * t), b1 = min(p.bh, b0 + segb);
+  auto count_of = [&](int b) { return p.cbase[b + 1] - p.cbase[b]; };
+  int g_sum = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int c = count_of(b);
+    g_sum += c / 2;
+    if (c & 1) {
+      const int n = n_chunks(nT);
+      a_units += n;
+      a_front += n_front_of(nT, n);
+      if (n > 1) {
+        a_slots += n;
+        a_comb += 1;
+      }
+    }
   }
-  if (threadIdx.x == 0) {
-    p.gbase[p.bh] = NG;
+  int NG;
+  int gb = block_exclusive_scan(g_sum, ws, &NG);
+  for (int b = b0; b < b1; ++b) {
+    p.gbase[b] = gb;
+    gb += count_of(b) / 2;
+  }
+  int nSU, nFront, nSP, nSC;
+  (void)block_exclusive_scan(a_units, ws, &nSU);
+  (void)block_exclusive_scan(a_front, ws, &nFront);
+  (void)block_exclusive_scan(a_slots, ws, &nSP);
+  (void)block_exclusive_scan(a_comb, ws, &nSC);
+  if (t == 0) {
     int chunk;
-    if (p.kv_chunk > 0) {
+    if (chunked) {
       chunk = p.kv_chunk;
     } else {
       int s = 1;
@@ -243,58 +336,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       s = min(s, max(1, nT / kMinChunk));
       chunk = (nT + s - 1) / s;
     }
-    chunk = max(1, min(chunk, max(nT, 1)));
+    chunk = max(1, min(chunk, nT));
     s_chunk_g = chunk;
     s_sg = (nT + chunk - 1) / chunk;
   }
   __syncthreads();
-  const int chunk_g = s_chunk_g, sg = (nT > 0) ? s_sg : 1;
-  const int chunk_s = (p.kv_chunk > 0) ? p.kv_chunk : INT_MAX;
-
-  // B: place G members, mark S rows with their chunk count.
-  for (int64_t r = r0; r < r1; ++r) {
-    const int len = len_of(r);
-    const int64_t b = r / nT;
-    const int e0 = p.E[b * nT];
-    const int fc = p.E[(b + 1) * nT] - e0;
-    int n = 0;
-    if (len == nT && nT > 0 && (p.E[r] - e0) < (fc / 2) * 2) {
-      const int j = p.E[r] - e0;
-      p.grows[(p.gbase[b] + j / 2) * 2 + (j & 1)] = (int)r;
-    } else {
-      n = (len <= 0) ? 1 : (int)((len + (int64_t)chunk_s - 1) / chunk_s);
-    }
-    p.sinfo[r] = n;
-  }
-  __syncthreads();
-
-  // C: scans of S units, S partial slots and S combine entries.
-  int c_su = 0, c_sp = 0, c_sc = 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const int n = p.sinfo[r];
-    c_su += n;
-    c_sp += (n > 1) ? n : 0;
-    c_sc += (n > 1);
-  }
-  int nSU, nSP, nSC;
-  (void)block_exclusive_scan(c_su, buf, &nSU);
-  int bp = block_exclusive_scan(c_sp, buf, &nSP);
-  int bc = block_exclusive_scan(c_sc, buf, &nSC);
-  for (int64_t r = r0; r < r1; ++r) {
-    const int n = p.sinfo[r];
-    p.sp[r] = bp;
-    p.sc[r] = bc;
-    bp += (n > 1) ? n : 0;
-    bc += (n > 1);
-  }
-  __syncthreads();
-
+  const int chunk_g = s_chunk_g, sg = s_sg;
   const int64_t nGU = (int64_t)NG * sg;
   const int64_t gslots = (sg > 1) ? 2 * nGU : 0;
   const int64_t n_units = nGU + nSU;
   const int64_t n_comb = ((sg > 1) ? 2LL * NG : 0) + nSC;
   if (n_units > p.max_units || gslots + nSP > p.max_slots) {
-    if (threadIdx.x == 0) {
+    if (t == 0) {
       p.hdr->n_units = 0;
       p.hdr->n_comb = 0;
       p.hdr->overflow = 1;
@@ -303,88 +356,131 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     }
     return;
   }
+  // From here every count fits in 32 bits (bounded by max_units / max_slots).
 
-  // D: unit order.  S units of at least half a full row (complete rows left
-  // over from the pairing) come first, so that no unit as long as a G unit
-  // starts late; then the G units; then the other S units in row order, so
-  // that neighbouring query tiles, whose key windows overlap, run close in
-  // time on one XCD and share its L2.
-  __shared__ int s_front;
-  if (threadIdx.x == 0) s_front = 0;
-  auto s_unit_len = [&](int len, int n, int c) {
-    const int ch = (n > 1) ? chunk_s : max(len, 0);
-    return max(0, min(len, (c + 1) * ch) - c * ch);
-  };
-  auto is_front = [&](int lu) { return 2 * lu >= nT && nT > 0; };
-  int c_rest = 0, c_front = 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const int n = p.sinfo[r];
-    const int len = len_of(r);
-    for (int c = 0; c < n; ++c) {
-      if (is_front(s_unit_len(len, n, c)))
-        ++c_front;
-      else
-        ++c_rest;
+  // Unit order: S units of at least half a full row first (complete rows left
+  // over from the pairing), so that no unit as long as a G unit starts late;
+  // then the G units; then the other S units in row order, so that
+  // neighbouring query tiles, whose key windows overlap, run close in time on
+  // one XCD and share its L2.
+  const int ngu = (int)nGU, gsl = (int)gslots;
+  const int rest_base = nFront + ngu;
+  const int comb_base = (sg > 1) ? 2 * NG : 0;
+
+  // pass 2: place every row
+  int carry_rest = 0, carry_slot = 0, carry_comb = 0;
+  carry_c = 0;
+  for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
+    const int r0 = c0 + kPlanSeg * t;
+    int len[kPlanSeg];
+    load_lengths(p.row_ptr, rows, r0, len);
+    int n_c = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanSeg; ++j) n_c += (len[j] == nT);
+    int blk_c;
+    int e = carry_c + block_exclusive_scan(n_c, ws, &blk_c);
+    // pairing data of the segment's first (b, h), which every row shares but
+    // those past a (b, h) boundary
+    const int bf = min(r0, rows - 1) / nT;
+    const int cb_f = p.cbase[bf], cnt_f = p.cbase[bf + 1] - cb_f, gb_f = p.gbase[bf];
+    int b = bf, pos = min(r0, rows - 1) - bf * nT;
+    int nS[kPlanSeg];  // S chunks of the row, 0 for G members and padding
+    int v_rest = 0, v_slot = 0, v_comb = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanSeg; ++j) {
+      nS[j] = 0;
+      if (len[j] >= 0) {
+        bool g_member = false;
+        if (len[j] == nT) {
+          const int cb_r = (b == bf) ? cb_f : p.cbase[b];
+          const int cnt_r = (b == bf) ? cnt_f : p.cbase[b + 1] - cb_r;
+          const int gb_r = (b == bf) ? gb_f : p.gbase[b];
+          const int jj = e - cb_r;  // index among the complete rows of (b, h)
+          ++e;
+          if (jj < (cnt_r / 2) * 2) {
+            p.grows[(gb_r + jj / 2) * 2 + (jj & 1)] = r0 + j;
+            g_member = true;
+          }
+        }
+        if (!g_member) {
+          const int n = n_chunks(len[j]);
+          nS[j] = n;
+          v_rest += n - n_front_of(len[j], n);
+          if (n > 1) {
+            v_slot += n;
+            v_comb += 1;
+          }
+        }
+      }
+      if (++pos == nT) {
+        pos = 0;
+        ++b;
+      }
     }
+    int blk_rest, blk_slot, blk_comb;
+    int pos_rest = carry_rest + block_exclusive_scan(v_rest, ws, &blk_rest);
+    int pos_slot = carry_slot + block_exclusive_scan(v_slot, ws, &blk_slot);
+    int pos_comb = carry_comb + block_exclusive_scan(v_comb, ws, &blk_comb);
+#pragma unroll
+    for (int j = 0; j < kPlanSeg; ++j) {
+      const int n = nS[j];
+      if (n == 0) continue;
+      const int r = r0 + j;
+      for (int c = 0; c < n; ++c) {
+        Unit u;
+        u.row[0] = r;
+        u.row[1] = -1;
+        u.kb = (n > 1) ? c * chunk_s : 0;
+        u.ke = u.kb + chunk_len(len[j], n, c);
+        u.slot = (n > 1) ? gsl + pos_slot + c : -1;
+        u.mode = 1;
+        u.pad[0] = u.pad[1] = 0;
+        const int at = is_front(u.ke - u.kb) ? atomicAdd(&s_front, 1) : rest_base + pos_rest++;
+        p.units[at] = u;
+      }
+      if (n > 1) {
+        Comb cb2;
+        cb2.row = r;
+        cb2.slot0 = gsl + pos_slot;
+        cb2.stride = 1;
+        cb2.n = n;
+        p.comb[comb_base + pos_comb] = cb2;
+        pos_slot += n;
+        ++pos_comb;
+      }
+    }
+    carry_c += blk_c;
+    carry_rest += blk_rest;
+    carry_slot += blk_slot;
+    carry_comb += blk_comb;
   }
-  int n_rest, n_front;
-  int rest_pos = block_exclusive_scan(c_rest, buf, &n_rest);
-  (void)block_exclusive_scan(c_front, buf, &n_front);
-  const int64_t rest_base = (int64_t)n_front + nGU;
+  __syncthreads();
 
-  // emit units and combine entries
-  for (int64_t i = threadIdx.x; i < nGU; i += kPlanThreads) {
-    const int gi = (int)(i / sg), c = (int)(i % sg);
+  // G units (their rows were placed in grows by pass 2) and their combine entries
+  for (int i = t; i < ngu; i += kPlanThreads) {
+    const int gi = i / sg, c = i - gi * sg;
     Unit u;
     u.row[0] = p.grows[2 * gi];
     u.row[1] = p.grows[2 * gi + 1];
     u.kb = c * chunk_g;
     u.ke = min(nT, u.kb + chunk_g);
-    u.slot = (sg > 1) ? (int)(2 * i) : -1;
+    u.slot = (sg > 1) ? 2 * i : -1;
     u.mode = 0;
     u.pad[0] = u.pad[1] = 0;
-    p.units[n_front + i] = u;
+    p.units[nFront + i] = u;
   }
   if (sg > 1) {
-    for (int64_t i = threadIdx.x; i < 2LL * NG; i += kPlanThreads) {
-      const int gi = (int)(i / 2), q = (int)(i & 1);
-      Comb cb;
-      cb.row = p.grows[2 * gi + q];
-      cb.slot0 = 2 * gi * sg + q;
-      cb.stride = 2;
-      cb.n = sg;
-      p.comb[i] = cb;
+    for (int i = t; i < 2 * NG; i += kPlanThreads) {
+      const int gi = i >> 1, q = i & 1;
+      Comb cb2;
+      cb2.row = p.grows[2 * gi + q];
+      cb2.slot0 = 2 * gi * sg + q;
+      cb2.stride = 2;
+      cb2.n = sg;
+      p.comb[i] = cb2;
     }
   }
-  const int64_t comb_base = (sg > 1) ? 2LL * NG : 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const int n = p.sinfo[r];
-    if (n == 0) continue;
-    const int len = len_of(r);
-    const int ch = (n > 1) ? chunk_s : max(len, 0);
-    for (int c = 0; c < n; ++c) {
-      Unit u;
-      u.row[0] = (int)r;
-      u.row[1] = -1;
-      u.kb = c * ch;
-      u.ke = u.kb + s_unit_len(len, n, c);
-      u.slot = (n > 1) ? (int)(gslots + p.sp[r] + c) : -1;
-      u.mode = 1;
-      u.pad[0] = u.pad[1] = 0;
-      const int64_t pos = is_front(u.ke - u.kb) ? (int64_t)atomicAdd(&s_front, 1)
-                                                : rest_base + rest_pos++;
-      p.units[pos] = u;
-    }
-    if (n > 1) {
-      Comb cb;
-      cb.row = (int)r;
-      cb.slot0 = (int)(gslots + p.sp[r]);
-      cb.stride = 1;
-      cb.n = n;
-      p.comb[comb_base + p.sc[r]] = cb;
-    }
-  }
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     p.hdr->n_units = (int)n_units;
     p.hdr->n_comb = (int)n_comb;
     p.hdr->chunks_g = sg;
@@ -926,12 +1022,9 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   pa.max_units = L.max_units;
   pa.max_slots = L.max_slots;
   pa.hdr = hdr;
-  pa.E = reinterpret_cast<int*>(w + L.off_E);
+  pa.cbase = reinterpret_cast<int*>(w + L.off_cbase);
   pa.gbase = reinterpret_cast<int*>(w + L.off_gbase);
   pa.grows = reinterpret_cast<int*>(w + L.off_grows);
-  pa.sinfo = reinterpret_cast<int*>(w + L.off_sinfo);
-  pa.sp = reinterpret_cast<int*>(w + L.off_sp);
-  pa.sc = reinterpret_cast<int*>(w + L.off_sc);
   pa.ext = reinterpret_cast<int*>(w + L.off_ext);
   pa.nh = g.nh;
   pa.nw = g.nw;

@@ -11,8 +11,8 @@
 //                 first `dense_count` in (score desc by IEEE totalOrder, index
 //                 asc) are routed.  One thread per tile, the head's keys in LDS.
 //   2. lengths -- row length in closed form (nT if routed, else the clipped
-//                 window count), exclusive scan -> row_ptr.  One workgroup;
-//                 each thread scans a contiguous run of rows serially.
+//                 window count), exclusive scan -> row_ptr.  One workgroup,
+//                 rows in LDS-staged chunks, a block scan per chunk.
 //   3. fill    -- one wave per row writes the ascending key-tile list: 0..nT-1
 //                 for a routed row, else the window enumerated as runs of
 //                 consecutive tw for each (dt, dh), which is ascending tile order.
@@ -24,6 +24,7 @@ namespace {
 constexpr int kRouteThreads = 256;
 constexpr int kRouteChunk = 4096;   // keys staged in LDS per pass
 constexpr int kScanThreads = 1024;
+constexpr int kScanRowsPerThread = 8;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t b = __float_as_uint(f);
@@ -33,7 +34,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ scores,
                                                               uint8_t* __restrict__ routed,
                                                               int nT, int k) {
-  __shared__ uint32_t keys[kRouteChunk];
+  __shared__ uint4 keys4[kRouteChunk / 4];
+  uint32_t* keys = reinterpret_cast<uint32_t*>(keys4);
   const int bh = blockIdx.y;
   const int a = blockIdx.x * kRouteThreads + threadIdx.x;
   const float* sc = scores + (int64_t)bh * nT;
@@ -45,13 +47,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
   int ahead = 0;
   for (int base = 0; base < nT; base += kRouteChunk) {
     const int n = min(kRouteChunk, nT - base);
+    const int n4 = (n + 3) / 4;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kRouteThreads) keys[i] = order_key(sc[base + i]);
+    // up to 3 padding slots (last chunk only) hold 0: never greater than ka,
+    // and a tie would need an index below a - base < n, which they are not
+    for (int i = threadIdx.x; i < 4 * n4; i += kRouteThreads) keys[i] = (i < n) ? order_key(sc[base + i]) : 0u;
     __syncthreads();
     if (a < nT) {
-      for (int i = 0; i < n; ++i) {
-        const uint32_t kb = keys[i];
-        ahead += (kb > ka) || (kb == ka && base + i < a);
+      // keys before position a - base win ties, keys after it lose them
+      const int split = a - base;
+#pragma unroll 8
+      for (int i4 = 0; i4 < n4; ++i4) {
+        const uint4 kb = keys4[i4];
+        const int i = 4 * i4;
+        ahead += (kb.x > ka) || (kb.x == ka && i + 0 < split);
+        ahead += (kb.y > ka) || (kb.y == ka && i + 1 < split);
+        ahead += (kb.z > ka) || (kb.z == ka && i + 2 < split);
+        ahead += (kb.w > ka) || (kb.w == ka && i + 3 < split);
       }
     }
   }
@@ -73,37 +85,62 @@ __device__ int window_count(int tt, int th, int tw, int r, int nt, int nh, int n
   return total;
 }
 
-__device__ __forceinline__ int row_length(int64_t row, const uint8_t* routed, const uint8_t* radii,
-                                          int r_max, int nt, int nh, int nw, int nT) {
-  if (routed[row]) return nT;
+__device__ __forceinline__ int row_length(int64_t row, bool is_routed, int radius, int r_max, int nt,
+                                          int nh, int nw, int nT) {
+  if (is_routed) return nT;
   const int a = (int)(row % nT);
-  const int r = min((int)radii[row], r_max);
+  const int r = min(radius, r_max);
   return window_count(a / (nh * nw), (a / nw) % nh, a % nw, r, nt, nh, nw);
 }
 
+// Row lengths and their exclusive scan.  Rows are taken in chunks of
+// kScanRowsPerThread * kScanThreads: the chunk's routed flags and radii are
+// staged in LDS with coalesced loads, each thread computes the lengths of
+// kScanRowsPerThread consecutive rows, and a block scan of the per-thread sums
+// (plus the running total of earlier chunks) gives row_ptr.
 __global__ __launch_bounds__(kScanThreads) void lengths_scan_kernel(
     const uint8_t* __restrict__ routed, const uint8_t* __restrict__ radii, int r_max,
     int64_t rows, int nt, int nh, int nw, int* __restrict__ row_ptr) {
+  constexpr int kChunk = kScanRowsPerThread * kScanThreads;
   __shared__ int sums[kScanThreads];
-  const int64_t seg = (rows + kScanThreads - 1) / kScanThreads;
-  const int64_t r0 = min(rows, seg * threadIdx.x), r1 = min(rows, r0 + seg);
+  __shared__ uint8_t s_rt[kChunk], s_rad[kChunk];
   const int nT = nt * nh * nw;
-  int local = 0;
-  for (int64_t r = r0; r < r1; ++r) local += row_length(r, routed, radii, r_max, nt, nh, nw, nT);
-  sums[threadIdx.x] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 per-thread sums.
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = (threadIdx.x >= off) ? sums[threadIdx.x - off] : 0;
+  const int t = threadIdx.x;
+  if (t == 0) row_ptr[0] = 0;
+  int carry = 0;
+  for (int64_t c0 = 0; c0 < rows; c0 += kChunk) {
+    const int n = (int)min<int64_t>(kChunk, rows - c0);
+    for (int i = t; i < n; i += kScanThreads) {
+      s_rt[i] = routed[c0 + i];
+      s_rad[i] = radii[c0 + i];
+    }
     __syncthreads();
-    sums[threadIdx.x] += v;
+    int len[kScanRowsPerThread];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < kScanRowsPerThread; ++j) {
+      const int i = kScanRowsPerThread * t + j;
+      len[j] = (i < n) ? row_length(c0 + i, s_rt[i] != 0, s_rad[i], r_max, nt, nh, nw, nT) : 0;
+      local += len[j];
+    }
+    sums[t] = local;
     __syncthreads();
-  }
-  int run = sums[threadIdx.x] - local;  // exclusive prefix of this thread's run
-  if (threadIdx.x == 0) row_ptr[0] = 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    run += row_length(r, routed, radii, r_max, nt, nh, nw, nT);
-    row_ptr[r + 1] = run;
+    // Hillis-Steele inclusive scan over the per-thread sums.
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+      const int v = (t >= off) ? sums[t - off] : 0;
+      __syncthreads();
+      sums[t] += v;
+      __syncthreads();
+    }
+    int run = carry + sums[t] - local;
+#pragma unroll
+    for (int j = 0; j < kScanRowsPerThread; ++j) {
+      const int i = kScanRowsPerThread * t + j;
+      run += len[j];
+      if (i < n) row_ptr[c0 + i + 1] = run;
+    }
+    carry += sums[kScanThreads - 1];
+    __syncthreads();
   }
 }
 

@@ -46,8 +46,8 @@ __device__ __forceinline__ uint64_t tile_valid_mask(int tau, int nh, int nw, int
 
 struct AttnLayout {
   int64_t rows, bh, max_units, max_slots;
-  size_t off_E, off_gbase, off_grows, off_sinfo, off_sp, off_sc, off_units, off_comb,
-      off_po, off_pml, off_ext, total;
+  size_t off_cbase, off_gbase, off_grows, off_units, off_comb, off_po, off_pml, off_ext,
+      total;
 };
 
 // Launchers (one per source file); each returns the launch status.
