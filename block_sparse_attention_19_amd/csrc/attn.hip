@@ -71,11 +71,14 @@ struct Comb {
   int32_t row, slot0, stride, n;
 };
 
-// Units are dealt to 8 queues in chunks of kQueueChunk consecutive units
-// (queue x owns units u with (u / kQueueChunk) % 8 == x).  Workgroup b serves
-// queue b % 8 first, the XCD that the hardware dispatches it to, so
-// neighbouring query tiles (overlapping key windows, the same head's K/V)
-// share that XCD's L2; an empty queue sends its workgroups to the others.
+// Units are dealt to 8 queues, one per XCD: workgroup b serves queue b % 8
+// first, the XCD that the hardware dispatches it to, and an empty queue sends
+// its workgroups to the others.  The head of the order (long units: front S
+// and G units) is dealt in chunks of kQueueChunk consecutive units (queue x
+// owns units u with (u / kQueueChunk) % 8 == x), which balances the long
+// units; the rest (local rows, in row order) is cut into 8 contiguous spans,
+// so that the units running at once on an XCD are neighbouring query tiles
+// whose key windows overlap and share its L2.
 constexpr int kQueues = 8;
 constexpr int kQueueChunk = 16;
 
@@ -85,9 +88,12 @@ struct Header {
   int32_t n_comb;
   int32_t chunks_g;
   int32_t overflow;
-  int32_t pad0[3];
+  int32_t n_head;      // units [0, n_head): front S and G units, dealt in chunks
+  int32_t rest_span;   // units past n_head: queue x owns n_head + [x, x + 1) * rest_span
+  int32_t pad0;
   int32_t queue[kQueues];
-  int32_t pad[48];
+  int32_t queue_rest[kQueues];
+  int32_t pad[40];
 };
 static_assert(sizeof(Header) == 256, "header layout");
 
@@ -352,7 +358,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       p.hdr->n_comb = 0;
       p.hdr->overflow = 1;
       p.hdr->counter = 0;
-      for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = 0;
+      p.hdr->n_head = 0;
+      p.hdr->rest_span = 0;
+      for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = p.hdr->queue_rest[x] = 0;
     }
     return;
   }
@@ -486,7 +494,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     p.hdr->chunks_g = sg;
     p.hdr->overflow = 0;
     p.hdr->counter = 0;
-    for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = 0;
+    p.hdr->n_head = nFront + ngu;
+    p.hdr->rest_span = ((int)n_units - (nFront + ngu) + kQueues - 1) / kQueues;
+    for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = p.hdr->queue_rest[x] = 0;
   }
 }
 
@@ -831,26 +841,42 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_unit;
+  __shared__ int s_head_done;  // this workgroup found the head of the order empty
   const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
   const int q = lane & 31, h = lane >> 5;
   const int nT = args.nT;
   const int n_units = args.hdr->n_units;
+  const int n_head = args.hdr->n_head;
+  const int rest_span = args.hdr->rest_span;
   const int half = wave & 1;
   const int grp = wave >> 1;  // G: which query tile; S: which key split
   const int home = blockIdx.x % kQueues;
   constexpr int TC = Cfg<D>::kTileChunks;
 
+  if (tid == 0) s_head_done = 0;
   for (;;) {
     if (tid == 0) {
       int u = -1;
-      for (int k = 0; k < kQueues; ++k) {
+      for (int k = 0; k < kQueues && !s_head_done; ++k) {
         const int x = (home + k) % kQueues;
         const int idx = atomicAdd(&args.hdr_mut->queue[x], 1);
         const int cand = (idx / kQueueChunk) * (kQueues * kQueueChunk) + x * kQueueChunk +
                          idx % kQueueChunk;
-        if (cand < n_units) {
+        if (cand < n_head) {
           u = cand;
           break;
+        }
+      }
+      if (u < 0) {
+        s_head_done = 1;
+        for (int k = 0; k < kQueues; ++k) {
+          const int x = (home + k) % kQueues;
+          const int idx = atomicAdd(&args.hdr_mut->queue_rest[x], 1);
+          const int cand = n_head + x * rest_span + idx;
+          if (idx < rest_span && cand < n_units) {
+            u = cand;
+            break;
+          }
         }
       }
       s_unit = u;
