@@ -565,6 +565,14 @@ struct WaveState {
   float l;  // this lane's partial sum of P
 };
 
+// This wave's Q fragments (B operands of S^T = K Q^T): row q of its 32 query
+// rows, 8 features per 16-feature k-step (lane half h takes the upper 8).
+template <int D>
+__device__ __forceinline__ void load_q(WaveState<D>& st, const uint16_t* qp) {
+#pragma unroll
+  for (int t = 0; t < Cfg<D>::kKSteps; ++t) st.qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
+}
+
 // S^T (32 keys x 32 queries) = K Q^T for this wave's 32 query rows, from a
 // block of 32 consecutive K rows (`k32`: row i of the block at i * 2D bytes,
 // swizzled as k_off).
@@ -739,12 +747,14 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int
 template <int D>
 __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const int* cols,
                                             int nkeys, const char* kbase, const char* vbase,
-                                            const AttnArgs& a, int wave, int lane) {
+                                            const AttnArgs& a, int wave, int lane,
+                                            const uint16_t* qp) {
   constexpr int TB = Cfg<D>::kTileBytes;
   const int j0 = uni(cols[0]);
   int jn = (1 < nkeys) ? uni(cols[1]) : -1;
   int code = uni(a.ext[j0]);
   dma_tile<D>(smem, kbase + (int64_t)j0 * TB, vbase + (int64_t)j0 * TB, wave, 4, lane);
+  load_q<D>(st, qp);  // in flight with the first tile; one wait covers both
   wait_dma();
   lds_barrier();
   for (int step = 0; step < nkeys; step += 2) {
@@ -797,7 +807,8 @@ __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const cha
 template <int D>
 __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const int* cols,
                                             int nkeys, const char* kbase, const char* vbase,
-                                            const AttnArgs& a, int wave, int lane, int grp) {
+                                            const AttnArgs& a, int wave, int lane, int grp,
+                                            const uint16_t* qp) {
   constexpr int TB = Cfg<D>::kTileBytes;
   constexpr int KH = 32 * Cfg<D>::kRowBytes;
   constexpr int BUF = KH + D * 64;                       // one half-tile buffer
@@ -809,6 +820,7 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
   int jn = (2 + grp < nkeys) ? uni(cols[2 + grp]) : -1;
   int code = (j >= 0) ? uni(a.ext[j]) : 0;
   if (j >= 0) dma_half<D>(region, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, 0, wi, 2, lane);
+  load_q<D>(st, qp);  // in flight with the first half tile; one wait covers both
   wait_dma();
   lds_barrier();
   for (int i = 0; i < nsteps; ++i) {
@@ -857,7 +869,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   for (;;) {
     if (tid == 0) {
       int u = -1;
-      for (int k = 0; k < kQueues && !s_head_done; ++k) {
+      for (int k = 0; k < kQueues && !s_head_done && u < 0; ++k) {
         const int x = (home + k) % kQueues;
         const int idx = atomicAdd(&args.hdr_mut->queue[x], 1);
         const int cand = (idx / kQueueChunk) * (kQueues * kQueueChunk) + x * kQueueChunk +
@@ -869,7 +881,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
       }
       if (u < 0) {
         s_head_done = 1;
-        for (int k = 0; k < kQueues; ++k) {
+        for (int k = 0; k < kQueues && u < 0; ++k) {
           const int x = (home + k) % kQueues;
           const int idx = atomicAdd(&args.hdr_mut->queue_rest[x], 1);
           const int cand = n_head + x * rest_span + idx;
@@ -898,16 +910,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     const int64_t qrow0 = (int64_t)row * kTileTokens + 32 * half;
 
     WaveState<D> st;
-    {
-      const uint16_t* qp = args.q + (qrow0 + q) * D + 8 * h;
-#pragma unroll
-      for (int t = 0; t < Cfg<D>::kKSteps; ++t)
-        st.qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
-      // Q must be complete before the key loop: otherwise the wait counts the
-      // compiler derives inside the loop also cover the tile prefetches and
-      // stall Q.K^T on them.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    }
+    const uint16_t* qp = args.q + (qrow0 + q) * D + 8 * h;
 #pragma unroll
     for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
 #pragma unroll
@@ -920,9 +923,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     const char* kbase = reinterpret_cast<const char*>(args.k) + bh * (int64_t)nT * TC * 16;
     const char* vbase = reinterpret_cast<const char*>(args.v) + bh * (int64_t)nT * TC * 16;
     if (g_mode)
-      run_steps_g<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane);
+      run_steps_g<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane, qp);
     else
-      run_steps_s<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane, grp);
+      run_steps_s<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane, grp, qp);
 
     // S units: merge the two key splits (waves 2,3 -> waves 0,1) through LDS.
     if (!g_mode) {
