@@ -262,3 +262,63 @@ def window_count_closed_form(r: int) -> int:
     """Key tiles kept by an interior (unclipped) query tile of radius r:
     sum over dt in [-r, r] of the (2(r-|dt|)+1)^2 spatial square."""
     return sum((2 * (r - abs(dt)) + 1) ** 2 for dt in range(-r, r + 1))
+
+
+# ------------------------------------------- token-level inputs -> tile inputs
+#
+# TRA's pipeline produces one budget and one radius per query *token* (steps 1
+# and 2) and translates the token-level radii into block masks (step 3);
+# HetA-DiT predicts a difficulty per token.  The block mask above takes one
+# radius and one routing score per query *tile*.  These functions make the
+# connection, with the readings: budgets count key tokens; a token's radius is
+# the smallest r in [0, r_max] whose tile window (the rule of tile_keep) holds
+# at least its budget of real key tokens, r_max if none does; a tile's radius
+# is the largest radius among its real tokens (its window then contains every
+# token's window); a tile's routing score is the largest score among its real
+# tokens in the IEEE-754 total order (the tile is routed if any of its tokens
+# is among the most uncertain).  Per-token arrays are [N] in raster order.
+
+def tile_valid_tokens(T: int, H: int, W: int) -> np.ndarray:
+    """int64 [nT]: real (non-padding) tokens of every tile, by counting."""
+    return np.bincount(token_tile(T, H, W), minlength=num_tiles(T, H, W)).astype(np.int64)
+
+
+def window_tokens(radius: int, T: int, H: int, W: int) -> np.ndarray:
+    """int64 [nT]: real key tokens inside the local window of each query tile
+    when every tile has radius `radius` and none is routed (brute force over
+    the tile_keep matrix)."""
+    n = num_tiles(T, H, W)
+    keep = tile_keep(np.full(n, radius, dtype=np.int64), np.zeros(n, dtype=bool), T, H, W)
+    return keep.astype(np.int64) @ tile_valid_tokens(T, H, W)
+
+
+def budget_to_radius(budget: np.ndarray, r_max: int, T: int, H: int, W: int) -> np.ndarray:
+    """TRA step 2 (budget -> base radius): uint8 [N] radius per query token for
+    int [N] token budgets."""
+    tt = token_tile(T, H, W)
+    counts = np.stack([window_tokens(r, T, H, W) for r in range(r_max + 1)])  # [r_max+1, nT]
+    enough = counts[:, tt] >= np.asarray(budget, dtype=np.int64)[None, :]
+    radius = np.where(enough.any(axis=0), enough.argmax(axis=0), r_max)
+    return radius.astype(np.uint8)
+
+
+def tile_radius_from_tokens(token_radius: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
+    """TRA step 3 (token-level radii -> block mask input): uint8 [nT], the
+    largest radius among each tile's real tokens."""
+    out = np.zeros(num_tiles(T, H, W), dtype=np.uint8)
+    np.maximum.at(out, token_tile(T, H, W), np.asarray(token_radius, dtype=np.uint8))
+    return out
+
+
+def tile_score_from_tokens(token_score: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
+    """HetA-DiT routing at tile granularity: float32 [nT], the token score of
+    each tile that is largest in the IEEE-754 total order."""
+    s = np.asarray(token_score, dtype=np.float32)
+    key = total_order_key(s).astype(np.int64)
+    tt = token_tile(T, H, W)
+    best = np.full(num_tiles(T, H, W), -1, dtype=np.int64)
+    np.maximum.at(best, tt, key)
+    out = np.empty(num_tiles(T, H, W), dtype=np.float32)
+    for a in range(out.size):  # the token holding the best key (keys are a bijection)
+        out[a] = s[np.flatnonzero((tt == a) & (key == best[a]))[0]]
+    return out
