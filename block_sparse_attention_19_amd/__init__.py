@@ -7,7 +7,8 @@ pointers and the current HIP stream, and turns status codes into exceptions.
 There is no CPU fallback: without the built library every call raises.
 
 Functions mirror the C entry points:
-    tile_permute, tile_unpermute, mask_nnz_bound, build_mask, attn_fwd
+    tile_permute, tile_unpermute, mask_nnz_bound, build_mask, attn_fwd,
+    budget_to_radius, tile_radius_from_tokens, tile_score_from_tokens
 plus ``attention``, which composes them into one block-sparse attention call.
 """
 from __future__ import annotations
@@ -64,6 +65,9 @@ def lib() -> ctypes.CDLL:
         "vsa_mask_nnz_bound": (I64, [SP, I32, I32]),
         "vsa_mask_workspace_bytes": (SZ, [SP]),
         "vsa_build_mask": (ctypes.c_int, [SP, P, P, I32, I32, P, P, I64, P, P, SZ, P]),
+        "vsa_budget_to_radius": (ctypes.c_int, [SP, P, I32, P, P]),
+        "vsa_tile_radius_from_tokens": (ctypes.c_int, [SP, P, P, P]),
+        "vsa_tile_score_from_tokens": (ctypes.c_int, [SP, P, P, P]),
         "vsa_attn_workspace_bytes": (SZ, [SP, I32]),
         "vsa_attn_fwd": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, I32, P, SZ, P]),
     }
@@ -180,6 +184,52 @@ def build_mask(radii: torch.Tensor, scores: torch.Tensor, s: Shape, dense_count:
                                 _ptr(ws), ws_bytes if ws is not None else 0, _stream(dev)),
            "vsa_build_mask")
     return row_ptr, col_idx, routed
+
+
+def _token_array(x: torch.Tensor, s: Shape, dtype: torch.dtype, name: str) -> torch.Tensor:
+    x = _require(x, dtype, name)
+    if x.shape != (s.batch, s.heads, s.T * s.H * s.W):
+        raise ValueError(f"{name} must be [B, heads, T*H*W], got {tuple(x.shape)}")
+    return x
+
+
+def budget_to_radius(budget: torch.Tensor, s: Shape, r_max: int,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int32 key budgets per query token [B, heads, N] -> uint8 radii [B, heads, N]
+    (the smallest tile radius whose window holds the budget, capped at r_max)."""
+    budget = _token_array(budget, s, torch.int32, "budget")
+    if out is None:
+        out = torch.empty(budget.shape, dtype=torch.uint8, device=budget.device)
+    _check(lib().vsa_budget_to_radius(ctypes.byref(s), _ptr(budget), int(r_max), _ptr(out),
+                                      _stream(budget.device)), "vsa_budget_to_radius")
+    return out
+
+
+def tile_radius_from_tokens(token_radius: torch.Tensor, s: Shape,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """uint8 [B, heads, N] token radii -> uint8 [B, heads, nT] tile radii (max)."""
+    token_radius = _token_array(token_radius, s, torch.uint8, "token_radius")
+    if out is None:
+        out = torch.empty((s.batch, s.heads, num_tiles(s)), dtype=torch.uint8,
+                          device=token_radius.device)
+    _check(lib().vsa_tile_radius_from_tokens(ctypes.byref(s), _ptr(token_radius), _ptr(out),
+                                             _stream(token_radius.device)),
+           "vsa_tile_radius_from_tokens")
+    return out
+
+
+def tile_score_from_tokens(token_score: torch.Tensor, s: Shape,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """float32 [B, heads, N] token scores -> float32 [B, heads, nT] tile scores
+    (max in the IEEE-754 total order)."""
+    token_score = _token_array(token_score, s, torch.float32, "token_score")
+    if out is None:
+        out = torch.empty((s.batch, s.heads, num_tiles(s)), dtype=torch.float32,
+                          device=token_score.device)
+    _check(lib().vsa_tile_score_from_tokens(ctypes.byref(s), _ptr(token_score), _ptr(out),
+                                            _stream(token_score.device)),
+           "vsa_tile_score_from_tokens")
+    return out
 
 
 def attn_workspace_bytes(s: Shape, kv_chunk: int = 0) -> int:

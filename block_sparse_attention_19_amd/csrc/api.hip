@@ -215,6 +215,37 @@ vsa_status vsa_build_mask(const vsa_shape* s, const uint8_t* radii, const float*
                     "mask launch");
 }
 
+vsa_status vsa_budget_to_radius(const vsa_shape* s, const int32_t* budget, int32_t r_max,
+                                uint8_t* radius, void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(budget, 4, "budget"));
+  VSA_TRY(check_ptr(radius, 1, "radius"));
+  if (r_max < 0 || r_max > 255) {
+    set_error("r_max %d outside [0, 255]", r_max);
+    return VSA_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_budget_radius(*s, budget, r_max, radius, static_cast<hipStream_t>(stream)),
+                    "budget launch");
+}
+
+vsa_status vsa_tile_radius_from_tokens(const vsa_shape* s, const uint8_t* token_radius,
+                                       uint8_t* tile_radius, void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(token_radius, 1, "token_radius"));
+  VSA_TRY(check_ptr(tile_radius, 1, "tile_radius"));
+  return hip_status(launch_tile_radius(*s, token_radius, tile_radius, static_cast<hipStream_t>(stream)),
+                    "tile radius launch");
+}
+
+vsa_status vsa_tile_score_from_tokens(const vsa_shape* s, const float* token_score,
+                                      float* tile_score, void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(token_score, 4, "token_score"));
+  VSA_TRY(check_ptr(tile_score, 4, "tile_score"));
+  return hip_status(launch_tile_score(*s, token_score, tile_score, static_cast<hipStream_t>(stream)),
+                    "tile score launch");
+}
+
 size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk) {
   if (check_shape(s) != VSA_OK || kv_chunk < 0) return 0;
   return attn_layout(*s, kv_chunk).total;

@@ -55,6 +55,12 @@ hipError_t launch_permute(const vsa_shape& s, const void* x, void* xt, int layou
                           hipStream_t stream);
 hipError_t launch_unpermute(const vsa_shape& s, const void* xt, void* x, hipStream_t stream);
 size_t mask_workspace_bytes(const vsa_shape& s);
+hipError_t launch_budget_radius(const vsa_shape& s, const int* budget, int r_max, uint8_t* radius,
+                                hipStream_t stream);
+hipError_t launch_tile_radius(const vsa_shape& s, const uint8_t* token_radius, uint8_t* tile_radius,
+                              hipStream_t stream);
+hipError_t launch_tile_score(const vsa_shape& s, const float* token_score, float* tile_score,
+                             hipStream_t stream);
 hipError_t launch_build_mask(const vsa_shape& s, const uint8_t* radii, const float* scores,
                              int dense_count, int r_max, int* row_ptr, int* col_idx,
                              uint8_t* routed, void* ws, hipStream_t stream);

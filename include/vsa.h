@@ -137,6 +137,47 @@ vsa_status vsa_build_mask(const vsa_shape* s, const uint8_t* radii, const float*
                           int32_t* col_idx, int64_t col_capacity, uint8_t* routed,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ token-level inputs
+ * The mask builder takes one radius and one routing score per query tile.
+ * TRA produces a key budget and a radius per query *token* (steps 1-2) and
+ * translates token-level radii into block masks (step 3); HetA-DiT predicts a
+ * difficulty per token.  These three calls produce the tile inputs from
+ * per-token values.  Per-token arrays are [B][heads][N], N = T*H*W, tokens in
+ * raster order n = (t*H + h)*W + w.  The shape is validated as for the other
+ * calls (head_dim 64 or 128), though head_dim does not enter.
+ *
+ * vsa_budget_to_radius (TRA step 2, budget -> base radius):
+ *   budget   int32 [B][heads][N]: keys wanted by each query token (any int;
+ *            <= 0 asks for nothing beyond the own tile).
+ *   r_max    0 <= r_max <= 255.
+ *   radius   uint8 [B][heads][N]: the smallest r in [0, r_max] whose tile
+ *            window (|dt| <= r, max(|dh|,|dw|) <= r - |dt|, the rule of
+ *            vsa_build_mask) holds at least `budget` real key tokens; r_max
+ *            if none does.
+ * Errors: INVALID_ARG.
+ */
+vsa_status vsa_budget_to_radius(const vsa_shape* s, const int32_t* budget, int32_t r_max,
+                                uint8_t* radius, void* stream);
+
+/* vsa_tile_radius_from_tokens (TRA step 3, token radii -> tile radius):
+ *   token_radius uint8 [B][heads][N]
+ *   tile_radius  uint8 [B][heads][nT]: the largest radius among the tile's
+ *                real tokens, so the tile's window contains each token's.
+ * Errors: INVALID_ARG.
+ */
+vsa_status vsa_tile_radius_from_tokens(const vsa_shape* s, const uint8_t* token_radius,
+                                       uint8_t* tile_radius, void* stream);
+
+/* vsa_tile_score_from_tokens (HetA-DiT token difficulty -> tile routing score):
+ *   token_score float32 [B][heads][N], 4-byte aligned.
+ *   tile_score  float32 [B][heads][nT]: the tile's token score that is largest
+ *               in the IEEE-754 totalOrder (the order vsa_build_mask routes
+ *               by), so a tile is routed if any of its tokens ranks high.
+ * Errors: INVALID_ARG.
+ */
+vsa_status vsa_tile_score_from_tokens(const vsa_shape* s, const float* token_score,
+                                      float* tile_score, void* stream);
+
 /* -------------------------------------------------------------- attention
  * Device workspace (bytes) that vsa_attn_fwd needs for this shape and
  * kv_chunk (0 = automatic splitting).

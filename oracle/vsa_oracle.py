@@ -315,10 +315,8 @@ def tile_score_from_tokens(token_score: np.ndarray, T: int, H: int, W: int) -> n
     each tile that is largest in the IEEE-754 total order."""
     s = np.asarray(token_score, dtype=np.float32)
     key = total_order_key(s).astype(np.int64)
-    tt = token_tile(T, H, W)
     best = np.full(num_tiles(T, H, W), -1, dtype=np.int64)
-    np.maximum.at(best, tt, key)
-    out = np.empty(num_tiles(T, H, W), dtype=np.float32)
-    for a in range(out.size):  # the token holding the best key (keys are a bijection)
-        out[a] = s[np.flatnonzero((tt == a) & (key == best[a]))[0]]
-    return out
+    np.maximum.at(best, token_tile(T, H, W), key)
+    # back from the key to the float's bits (total_order_key inverted)
+    bits = np.where(best >= 2 ** 31, best - 2 ** 31, (~best) & 0xFFFFFFFF).astype(np.uint32)
+    return bits.view(np.float32)

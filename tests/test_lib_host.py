@@ -115,3 +115,22 @@ def test_overflow_is_reported():
 def test_workspace_grows_with_split():
     s = vsa.shape(1, 12, 128, 21, 30, 52)
     assert vsa.attn_workspace_bytes(s, 1) > vsa.attn_workspace_bytes(s, 0) > 0
+
+
+def test_token_calls_validate_before_launch():
+    L = vsa.lib()
+    s = vsa.shape(1, 2, 64, 8, 16, 16)
+    sp = ctypes.byref(s)
+    good = _p(0x10000)
+    assert L.vsa_budget_to_radius(sp, None, 3, good, None) == INVALID
+    assert L.vsa_budget_to_radius(sp, _p(0x10002), 3, good, None) == INVALID   # int32 misaligned
+    assert L.vsa_budget_to_radius(sp, good, -1, good, None) == INVALID
+    assert L.vsa_budget_to_radius(sp, good, 256, good, None) == INVALID
+    assert L.vsa_budget_to_radius(sp, good, 3, None, None) == INVALID
+    assert L.vsa_tile_radius_from_tokens(sp, None, good, None) == INVALID
+    assert L.vsa_tile_radius_from_tokens(sp, good, None, None) == INVALID
+    assert L.vsa_tile_score_from_tokens(sp, _p(0x10001), good, None) == INVALID
+    assert L.vsa_tile_score_from_tokens(sp, good, _p(0x10003), None) == INVALID
+    assert L.vsa_tile_score_from_tokens(None, good, good, None) == INVALID
+    s96 = vsa.shape(1, 2, 96, 8, 16, 16)
+    assert L.vsa_tile_radius_from_tokens(ctypes.byref(s96), good, good, None) == UNSUPPORTED

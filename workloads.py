@@ -22,7 +22,8 @@ order or in chunks):
   larger dot product, i.e. local attention mass);
 * stream 3: V ~ N(0, 1);
 * stream 4: one radius per cell, discrete-uniform over the config's set;
-* stream 5: one routing score per cell, U[0, 1) drawn in float64, stored float32.
+* stream 5: one routing score per cell, U[0, 1) drawn in float64, stored float32;
+* streams 6 / 7: per-token key budgets and routing scores (``token_inputs``).
 
 Q/K/V are drawn in float32 and rounded to bfloat16 (round to nearest even);
 they are returned as uint16 bit patterns, token-raster order
@@ -153,6 +154,23 @@ def radii_scores(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
     r = np.stack([head_radii(w, h) for h in range(w.heads)])[None]
     s = np.stack([head_scores(w, h) for h in range(w.heads)])[None]
     return np.ascontiguousarray(r), np.ascontiguousarray(s)
+
+
+# Per-token inputs of the token-level calls (budget -> radius, token radii /
+# scores -> tile radii / scores): stream 6 draws key budgets discrete-uniform
+# over [TOKEN_BUDGET_LO, TOKEN_BUDGET_HI] (roughly the key tokens of windows up
+# to radius 3 of an interior tile), stream 7 draws routing scores U[0, 1) in
+# float64, stored float32.  Layout [B=1, heads, N], raster token order.
+TOKEN_BUDGET_LO = 1
+TOKEN_BUDGET_HI = 8192
+
+
+def token_inputs(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
+    """Key budgets int32 [1, heads, N] and routing scores float32 [1, heads, N]."""
+    b = np.stack([_rng(w, 6, h).integers(TOKEN_BUDGET_LO, TOKEN_BUDGET_HI + 1, size=w.tokens)
+                  for h in range(w.heads)])[None].astype(np.int32)
+    s = np.stack([_rng(w, 7, h).random(w.tokens).astype(np.float32) for h in range(w.heads)])[None]
+    return np.ascontiguousarray(b), np.ascontiguousarray(s)
 
 
 def qkv(w: Workload, heads: Optional[range] = None):
