@@ -10,7 +10,9 @@ head_dim 128, radii in {1, 2, 3}, 20% of query tiles routed dense.
 Prints ONE JSON line.  ``value`` is retained-tile bf16 TFLOP/s of the whole
 step (kept tile pairs x 4*64*64*D flops over the step time); ``roofline``
 rates the attention kernel alone against the bf16 MFMA peak; ``cpu_baseline``
-times the fp64 CPU oracle on a bounded sample of the same workload.
+times the fp64 CPU oracle on a bounded sample of the same workload;
+``token_level_calls`` times the per-token -> per-tile calls (budget -> radius,
+tile radius, tile score) at the workload's size, outside the step.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 1]
 """
@@ -93,6 +95,45 @@ def cpu_baseline(w, q, k, v, r, s, kcount, budget_s):
             "sample": f"{done_tiles} query tiles ({pairs} retained tile pairs) of {w.name}, "
                       f"fp64 masked attention over all keys, {el:.1f} s; full-call "
                       f"extrapolation {el / max(done_tiles, 1) * w.heads * w.n_cells:.0f} s"}
+
+
+def token_level_calls(w, sh, dev, stream, reps):
+    """Time the token-level calls (budget -> radius per query token, token
+    radii / scores -> tile radii / scores) at the workload's size on its own
+    per-token draws; they are latency-bound, so report microseconds and the
+    HBM bytes they move."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_19_amd as vsa
+    import workloads as wl
+    budget, score = wl.token_inputs(w)
+    bd = torch.from_numpy(budget).to(dev)
+    sd = torch.from_numpy(score).to(dev)
+    r_max = 4
+    rad = torch.empty(budget.shape, dtype=torch.uint8, device=dev)
+    tr = torch.empty((1, w.heads, w.n_cells), dtype=torch.uint8, device=dev)
+    ts = torch.empty((1, w.heads, w.n_cells), dtype=torch.float32, device=dev)
+    calls = {
+        "budget_to_radius": (lambda: vsa.budget_to_radius(bd, sh, r_max, out=rad), 5),
+        "tile_radius_from_tokens": (lambda: vsa.tile_radius_from_tokens(rad, sh, out=tr), 1),
+        "tile_score_from_tokens": (lambda: vsa.tile_score_from_tokens(sd, sh, out=ts), 4),
+    }
+    out = {"r_max": r_max, "tokens_per_head": w.tokens, "heads": w.heads}
+    for name, (fn, in_bytes) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        n_tok = w.heads * w.tokens
+        moved = n_tok * in_bytes + (n_tok if name == "budget_to_radius" else w.heads * w.n_cells * (1 if "radius" in name else 4))
+        out[name] = {"us": round(us, 2), "hbm_bytes": int(moved), "GB/s": round(moved / (us * 1e-6) / 1e9, 1)}
+    return out
 
 
 def main():
@@ -200,6 +241,7 @@ def main():
         "breakdown_ms": {k2: round(v2, 4) for k2, v2 in per_stage.items()},
         "attn_valid_token_tflops": round(valid_flops / (attn_ms * 1e-3) / 1e12, 2),
     }
+    line["token_level_calls"] = token_level_calls(w, sh, dev, stream, args.steps)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, r, s, kcount, args.cpu_seconds)
     else:
