@@ -224,3 +224,37 @@ def test_attention_large_sampled(cid, ki):
     _check_sampled(w, q, k, v, r, s, kcount, out, heads=[0, w.heads - 1], seed=cid)
     del out
     torch.cuda.empty_cache()
+
+
+def test_attention_batch2_full():
+    """Two batch entries with different inputs, radii and scores (the
+    workloads draw B = 1; the batch axis stacks two draws)."""
+    T, H, W, heads, D = 9, 10, 11, 2, 64
+    ws = [wl.custom(T, H, W, heads, D, radius_set=(0, 1, 2), cid=c) for c in (410, 411)]
+    draws = [wl.qkv(w) + wl.radii_scores(w) for w in ws]
+    q, k, v, r, s = (np.concatenate([d[i] for d in draws], axis=0) for i in range(5))
+    w2 = ws[0].__class__(**{**ws[0].__dict__, "batch": 2})
+    for kcount in (0, 3):
+        say(f"attention batch=2 T={T} H={H} W={W} heads={heads} D={D} k={kcount}")
+        out = _run_all(w2, q, k, v, r, s, kcount)
+        keep, _ = vo.block_mask(r, s, kcount, T, H, W)
+        orp, oci = vo.csr(keep)
+        assert np.array_equal(out["rp"].cpu().numpy().astype(np.int64), orp)
+        assert np.array_equal(out["ci"][: int(orp[-1])].cpu().numpy().astype(np.int64), oci)
+        ref, _ = vo.attention(q, k, v, r, s, kcount, T, H, W, ws[0].scale)
+        assert_close(f64_of(out["o"]), ref, f"O batch=2 k={kcount}")
+
+
+@pytest.mark.parametrize("kv_chunk", [0, 4])
+def test_attention_d64_medium_split(kv_chunk):
+    """D = 64 with enough routed rows for G units and (kv_chunk 0) their
+    automatic key split, or a forced chunking of every row."""
+    T, H, W, heads, D = 21, 16, 16, 3, 64
+    w = wl.custom(T, H, W, heads, D, radius_set=(1, 2, 3), cid=412)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    kcount = 10
+    say(f"attention D=64 T={T} H={H} W={W} heads={heads} k={kcount} kv_chunk={kv_chunk}")
+    out = _run_all(w, q, k, v, r, s, kcount, kv_chunk=kv_chunk)
+    ref, _ = vo.attention(q, k, v, r, s, kcount, T, H, W, w.scale)
+    assert_close(f64_of(out["o"]), ref, f"O D=64 kv_chunk={kv_chunk}")
