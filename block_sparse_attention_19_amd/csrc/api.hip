@@ -78,6 +78,12 @@ vsa_status check_shape(const vsa_shape* s) {
     set_error("problem too large: %lld tile rows", (long long)rows);
     return VSA_ERR_OVERFLOW;
   }
+  // the permutes launch heads * nT workgroups of 256 threads in one grid
+  // dimension, whose work-item count is 32-bit
+  if ((int64_t)s->heads * nT * 256 > (int64_t)UINT32_MAX) {
+    set_error("problem too large: heads * tiles = %lld", (long long)(s->heads * nT));
+    return VSA_ERR_OVERFLOW;
+  }
   return VSA_OK;
 }
 

@@ -9,10 +9,11 @@
 // Three launches:
 //   1. route   -- rank of every tile's score within its (batch, head); the
 //                 first `dense_count` in (score desc by IEEE totalOrder, index
-//                 asc) are routed.  One thread per tile, the head's keys in LDS.
-//   2. lengths -- row length in closed form (nT if routed, else the clipped
-//                 window count), exclusive scan -> row_ptr.  One workgroup,
-//                 rows in LDS-staged chunks, a block scan per chunk.
+//                 asc) are routed.  Four threads per tile, the keys in LDS.
+//                 The row length in closed form (nT if routed, else the
+//                 clipped window count) goes to row_ptr[row + 1].
+//   2. scan    -- in-place exclusive scan of the lengths -> row_ptr.  One
+//                 workgroup, a shuffle block scan per chunk of rows.
 //   3. fill    -- one wave per row writes the ascending key-tile list: 0..nT-1
 //                 for a routed row, else the window enumerated as runs of
 //                 consecutive tw for each (dt, dh), which is ascending tile order.
@@ -31,45 +32,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ scores,
-                                                              uint8_t* __restrict__ routed,
-                                                              int nT, int k) {
-  __shared__ uint4 keys4[kRouteChunk / 4];
-  uint32_t* keys = reinterpret_cast<uint32_t*>(keys4);
-  const int bh = blockIdx.y;
-  const int a = blockIdx.x * kRouteThreads + threadIdx.x;
-  const float* sc = scores + (int64_t)bh * nT;
-  if (k == 0 || k == nT) {
-    if (a < nT) routed[(int64_t)bh * nT + a] = (k == nT) ? 1 : 0;
-    return;
-  }
-  const uint32_t ka = (a < nT) ? order_key(sc[a]) : 0u;
-  int ahead = 0;
-  for (int base = 0; base < nT; base += kRouteChunk) {
-    const int n = min(kRouteChunk, nT - base);
-    const int n4 = (n + 3) / 4;
-    __syncthreads();
-    // up to 3 padding slots (last chunk only) hold 0: never greater than ka,
-    // and a tie would need an index below a - base < n, which they are not
-    for (int i = threadIdx.x; i < 4 * n4; i += kRouteThreads) keys[i] = (i < n) ? order_key(sc[base + i]) : 0u;
-    __syncthreads();
-    if (a < nT) {
-      // keys before position a - base win ties, keys after it lose them
-      const int split = a - base;
-#pragma unroll 8
-      for (int i4 = 0; i4 < n4; ++i4) {
-        const uint4 kb = keys4[i4];
-        const int i = 4 * i4;
-        ahead += (kb.x > ka) || (kb.x == ka && i + 0 < split);
-        ahead += (kb.y > ka) || (kb.y == ka && i + 1 < split);
-        ahead += (kb.z > ka) || (kb.z == ka && i + 2 < split);
-        ahead += (kb.w > ka) || (kb.w == ka && i + 3 < split);
-      }
-    }
-  }
-  if (a < nT) routed[(int64_t)bh * nT + a] = (ahead < k) ? 1 : 0;
-}
-
 __device__ __forceinline__ int clip_count(int x, int s, int n) {
   return min(x + s, n - 1) - max(x - s, 0) + 1;
 }
@@ -85,61 +47,118 @@ __device__ int window_count(int tt, int th, int tw, int r, int nt, int nh, int n
   return total;
 }
 
-__device__ __forceinline__ int row_length(int64_t row, bool is_routed, int radius, int r_max, int nt,
-                                          int nh, int nw, int nT) {
-  if (is_routed) return nT;
-  const int a = (int)(row % nT);
-  const int r = min(radius, r_max);
-  return window_count(a / (nh * nw), (a / nw) % nh, a % nw, r, nt, nh, nw);
+// kRouteSplit threads share one tile: each counts the keys ahead of it in one
+// interleaved quarter of the staged keys (4-key vector reads), and the partial
+// counts are summed across the group with lane shuffles.
+constexpr int kRouteSplit = 4;
+
+// The tile's row length (nT if routed, else the clipped window count) is
+// written to row_ptr[row + 1] for the scan that follows.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ scores,
+                                                              const uint8_t* __restrict__ radii,
+                                                              uint8_t* __restrict__ routed,
+                                                              int* __restrict__ row_ptr, int k,
+                                                              int r_max, int nt, int nh, int nw) {
+  const int nT = nt * nh * nw;
+  __shared__ uint4 keys4[kRouteChunk / 4];
+  uint32_t* keys = reinterpret_cast<uint32_t*>(keys4);
+  const int bh = blockIdx.y;
+  const int part = threadIdx.x % kRouteSplit;
+  const int a = blockIdx.x * (kRouteThreads / kRouteSplit) + threadIdx.x / kRouteSplit;
+  const float* sc = scores + (int64_t)bh * nT;
+  const int64_t row = (int64_t)bh * nT + a;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) row_ptr[0] = 0;
+  auto finish = [&](bool is_routed) {
+    routed[row] = is_routed ? 1 : 0;
+    const int r = min((int)radii[row], r_max);
+    row_ptr[row + 1] = is_routed ? nT
+                                 : window_count(a / (nh * nw), (a / nw) % nh, a % nw, r, nt, nh, nw);
+  };
+  if (k == 0 || k == nT) {
+    if (a < nT && part == 0) finish(k == nT);
+    return;
+  }
+  const uint32_t ka = (a < nT) ? order_key(sc[a]) : 0u;
+  int ahead = 0;
+  for (int base = 0; base < nT; base += kRouteChunk) {
+    const int n = min(kRouteChunk, nT - base);
+    const int n4 = (n + 3) / 4;
+    __syncthreads();
+    // up to 3 padding slots (last chunk only) hold 0: never greater than ka,
+    // and a tie would need an index below a - base < n, which they are not
+    for (int i = threadIdx.x; i < 4 * n4; i += kRouteThreads) keys[i] = (i < n) ? order_key(sc[base + i]) : 0u;
+    __syncthreads();
+    if (a < nT) {
+      // keys before position a - base win ties, keys after it lose them
+      const int split = a - base;
+#pragma unroll 4
+      for (int i4 = part; i4 < n4; i4 += kRouteSplit) {
+        const uint4 kb = keys4[i4];
+        const int i = 4 * i4;
+        ahead += (kb.x > ka) || (kb.x == ka && i + 0 < split);
+        ahead += (kb.y > ka) || (kb.y == ka && i + 1 < split);
+        ahead += (kb.z > ka) || (kb.z == ka && i + 2 < split);
+        ahead += (kb.w > ka) || (kb.w == ka && i + 3 < split);
+      }
+    }
+  }
+  // the kRouteSplit threads of a tile are consecutive lanes of one wave
+#pragma unroll
+  for (int d = 1; d < kRouteSplit; d <<= 1) ahead += __shfl_xor(ahead, d);
+  if (a < nT && part == 0) finish(ahead < k);
 }
 
-// Row lengths and their exclusive scan.  Rows are taken in chunks of
-// kScanRowsPerThread * kScanThreads: the chunk's routed flags and radii are
-// staged in LDS with coalesced loads, each thread computes the lengths of
-// kScanRowsPerThread consecutive rows, and a block scan of the per-thread sums
-// (plus the running total of earlier chunks) gives row_ptr.
-__global__ __launch_bounds__(kScanThreads) void lengths_scan_kernel(
-    const uint8_t* __restrict__ routed, const uint8_t* __restrict__ radii, int r_max,
-    int64_t rows, int nt, int nh, int nw, int* __restrict__ row_ptr) {
+// In-place scan of the row lengths in row_ptr[1..rows] (row_ptr[0] = 0), so
+// that row_ptr becomes their exclusive scan.  Rows are taken in chunks of
+// kScanRowsPerThread * kScanThreads, each thread holding kScanRowsPerThread
+// consecutive lengths in registers; a block scan of the per-thread sums plus
+// the running total of earlier chunks gives each thread its offset.
+__global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(int64_t rows,
+                                                                    int* __restrict__ row_ptr) {
   constexpr int kChunk = kScanRowsPerThread * kScanThreads;
-  __shared__ int sums[kScanThreads];
-  __shared__ uint8_t s_rt[kChunk], s_rad[kChunk];
-  const int nT = nt * nh * nw;
+  __shared__ int sums[kScanThreads / 64];
   const int t = threadIdx.x;
-  if (t == 0) row_ptr[0] = 0;
+  const int lane = t & 63, wv = t >> 6;
+  int* len_p = row_ptr + 1;
   int carry = 0;
   for (int64_t c0 = 0; c0 < rows; c0 += kChunk) {
     const int n = (int)min<int64_t>(kChunk, rows - c0);
-    for (int i = t; i < n; i += kScanThreads) {
-      s_rt[i] = routed[c0 + i];
-      s_rad[i] = radii[c0 + i];
-    }
-    __syncthreads();
     int len[kScanRowsPerThread];
     int local = 0;
 #pragma unroll
     for (int j = 0; j < kScanRowsPerThread; ++j) {
       const int i = kScanRowsPerThread * t + j;
-      len[j] = (i < n) ? row_length(c0 + i, s_rt[i] != 0, s_rad[i], r_max, nt, nh, nw, nT) : 0;
+      len[j] = (i < n) ? len_p[c0 + i] : 0;
       local += len[j];
     }
-    sums[t] = local;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over the per-thread sums.
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-      const int v = (t >= off) ? sums[t - off] : 0;
-      __syncthreads();
-      sums[t] += v;
-      __syncthreads();
+    // lane shuffles within each wave, then a scan of the wave totals by the
+    // first wave
+    int x = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
     }
-    int run = carry + sums[t] - local;
+    if (lane == 63) sums[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+      int w_ = (lane < kScanThreads / 64) ? sums[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kScanThreads / 64; d <<= 1) {
+        const int y = __shfl_up(w_, d);
+        if (lane >= d) w_ += y;
+      }
+      if (lane < kScanThreads / 64) sums[lane] = w_;
+    }
+    __syncthreads();
+    int run = carry + ((wv > 0) ? sums[wv - 1] : 0) + x - local;
 #pragma unroll
     for (int j = 0; j < kScanRowsPerThread; ++j) {
       const int i = kScanRowsPerThread * t + j;
       run += len[j];
-      if (i < n) row_ptr[c0 + i + 1] = run;
+      if (i < n) len_p[c0 + i] = run;
     }
-    carry += sums[kScanThreads - 1];
+    carry += sums[kScanThreads / 64 - 1];
     __syncthreads();
   }
 }
@@ -193,10 +212,11 @@ hipError_t launch_build_mask(const vsa_shape& s, const uint8_t* radii, const flo
   const int bh = s.batch * s.heads;
   const int64_t rows = (int64_t)bh * g.nT;
   uint8_t* rt = routed ? routed : static_cast<uint8_t*>(ws);
-  dim3 rgrid((g.nT + kRouteThreads - 1) / kRouteThreads, bh);
-  route_kernel<<<rgrid, kRouteThreads, 0, stream>>>(scores, rt, g.nT, dense_count);
-  lengths_scan_kernel<<<1, kScanThreads, 0, stream>>>(rt, radii, r_max, rows, g.nt, g.nh, g.nw,
-                                                       row_ptr);
+  constexpr int kTilesPerBlock = kRouteThreads / kRouteSplit;
+  dim3 rgrid((g.nT + kTilesPerBlock - 1) / kTilesPerBlock, bh);
+  route_kernel<<<rgrid, kRouteThreads, 0, stream>>>(scores, radii, rt, row_ptr, dense_count,
+                                                    r_max, g.nt, g.nh, g.nw);
+  scan_lengths_kernel<<<1, kScanThreads, 0, stream>>>(rows, row_ptr);
   fill_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(rt, radii, r_max, rows, g.nt, g.nh,
                                                              g.nw, row_ptr, col_idx);
   return hipGetLastError();

@@ -3,8 +3,10 @@
 // "Token Radius Attention for Efficient Video Generation", pipeline step 3:
 // tokens are laid out tile-major so that every sparse support is a set of whole
 // 64-token blocks.  One workgroup moves one (batch, head, tile): the 64 slots of
-// a 4x4x4 tile, D features each.  Index arithmetic is done once per tile and
-// per slot (shifts only); the feature loop moves 16-byte chunks, so each token
+// a 4x4x4 tile, D features each.  Block x = tile * heads + head: consecutive
+// workgroups cover the heads of one tile, so each token's raster record (all
+// heads, contiguous) is streamed in one burst.  Index arithmetic is done once
+// per tile and per slot (shifts only); the feature loop moves 16-byte chunks, so each token
 // row is one contiguous 2*D-byte transfer on both sides.  Both directions are
 // HBM-bound: per tile they read and write 64*D*2 bytes (the padded side) or
 // valid*D*2 bytes (the raster side).
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void permute_token_major(
     int nw, int nT) {
   constexpr int C = D / 8;                 // 16-byte chunks per token row
   constexpr int kIters = kTileTokens * C / kThreads;
-  const int tau = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x % Hh, tau = blockIdx.x / Hh, b = blockIdx.y;
   const TileCoord o = tile_origin(tau, nh, nw);
   const int64_t N = (int64_t)T * H * W;
   uint4* dst = xt + (((int64_t)b * Hh + h) * nT + tau) * (kTileTokens * C);
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void permute_feature_major(
   constexpr int kIters = kTileTokens * C / kThreads;
   constexpr int kStride = D + 2;           // bf16 per LDS row; +2 staggers banks
   __shared__ uint16_t tile[kTileTokens * kStride];
-  const int tau = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x % Hh, tau = blockIdx.x / Hh, b = blockIdx.y;
   const TileCoord o = tile_origin(tau, nh, nw);
   const int64_t N = (int64_t)T * H * W;
 #pragma unroll
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_token_major(
     int nw, int nT) {
   constexpr int C = D / 8;
   constexpr int kIters = kTileTokens * C / kThreads;
-  const int tau = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x % Hh, tau = blockIdx.x / Hh, b = blockIdx.y;
   const TileCoord o = tile_origin(tau, nh, nw);
   const int64_t N = (int64_t)T * H * W;
   const uint4* src = xt + (((int64_t)b * Hh + h) * nT + tau) * (kTileTokens * C);
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_token_major(
 hipError_t launch_permute(const vsa_shape& s, const void* x, void* xt, int layout,
                           hipStream_t stream) {
   const Grid g = make_grid(s);
-  dim3 grid(g.nT, s.heads, s.batch);
+  dim3 grid(g.nT * s.heads, s.batch);
   const uint4* in = static_cast<const uint4*>(x);
   uint4* out = static_cast<uint4*>(xt);
   if (layout == VSA_LAYOUT_TOKEN_MAJOR) {
@@ -142,7 +144,7 @@ hipError_t launch_permute(const vsa_shape& s, const void* x, void* xt, int layou
 
 hipError_t launch_unpermute(const vsa_shape& s, const void* xt, void* x, hipStream_t stream) {
   const Grid g = make_grid(s);
-  dim3 grid(g.nT, s.heads, s.batch);
+  dim3 grid(g.nT * s.heads, s.batch);
   const uint4* in = static_cast<const uint4*>(xt);
   uint4* out = static_cast<uint4*>(x);
   if (s.head_dim == 128)
