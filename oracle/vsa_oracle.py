@@ -24,6 +24,12 @@ What is computed, and where it comes from:
   block-sparse execution of TRA step 3 and of the other pages skips masked
   tiles and must reach this same result.
 
+* Low-precision tier -- "Triage: Skip, Skim, or Refine Attention Tiles in
+  Video Diffusion Transformers": each kept tile pair is either computed in a
+  quick 4-bit version (skim) or fully (refine).  Reading adopted here: an
+  input tier per kept pair; a skim pair's scores use the MXFP4 (OCP MX v1.0)
+  round trips of q and k, the rest is unchanged.
+
 The oracle works on the valid tokens only (it has no padding); padded slots
 exist only in the tile-major layout.  All floating point is float64 on the
 exact bfloat16 input values.
@@ -221,6 +227,98 @@ def attention(q_bits, k_bits, v_bits, radii, scores, k: int, T: int, H: int, W: 
             vv = bf16_to_f64(v_bits[b, :, h])
             O[b, :, h], L[b, h] = attention_head_rows(q, kk, vv, keep[b, h], tt, rows, scale)
     return O, L
+
+
+# ------------------------------------------------ low-precision "skim" tiles
+#
+# "Triage: Skip, Skim, or Refine Attention Tiles in Video Diffusion
+# Transformers", plain-words summary and "Route by estimated error": every
+# tile is skipped, computed in a quick 4-bit version ("skim"), or computed
+# with extra correction ("refine").  The pages fix neither the 4-bit format,
+# nor which products it covers, nor the router's formulas.  Readings adopted
+# here: the tier is an input (one byte per kept tile pair, 1 = skim); the
+# 4-bit format is OCP Microscaling MXFP4 (E2M1 elements, one power-of-two E8M0
+# scale per block of 32 consecutive elements along the head dimension); a skim
+# pair takes its scores from the MXFP4-quantised q and k, everything after the
+# scores (softmax, P.V) as for a refine pair, which is the bf16 computation.
+
+MX_BLOCK = 32                      # elements sharing one scale
+E2M1_EMAX = 2                      # exponent of the largest E2M1 binade (4..6)
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # by code & 7
+
+
+def mxfp4_quantize(x: np.ndarray):
+    """MXFP4 encoding along the last axis (its length a multiple of 32), as the
+    OCP Microscaling Formats specification v1.0 defines it: the block scale is
+    X = 2^(floor(log2(max |v|)) - emax) with emax = 2 for E2M1 (exponent -127,
+    the smallest E8M0 value, for an all-zero block; clamped to [-127, 127]),
+    and each v / X is rounded to the nearest E2M1 value, ties to the even code,
+    magnitudes above 6 saturating to 6.
+
+    Returns (codes uint8 [..., n]: bit 3 sign, bits 0-2 the magnitude index into
+    E2M1_MAGNITUDES; exponents int32 [..., n/32]: X = 2^exponent)."""
+    x = np.asarray(x, dtype=np.float64)
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)                          # amax = f * 2^e, f in [0.5, 1)
+    expo = np.where(amax > 0, e - 1 - E2M1_EMAX, -127)
+    expo = np.clip(expo, -127, 127).astype(np.int32)
+    y = blocks / np.ldexp(1.0, expo)[..., None]
+    mag = np.abs(y)[..., None]
+    dist = np.abs(mag - E2M1_MAGNITUDES)           # [..., 32, 8]
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best                            # one or two nearest values
+    even = cand & ((np.arange(8) & 1) == 0)
+    idx = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    codes = (idx | np.where(np.signbit(y), 8, 0)).astype(np.uint8)
+    return codes.reshape(x.shape), expo
+
+
+def mxfp4_dequantize(codes: np.ndarray, expo: np.ndarray) -> np.ndarray:
+    """Values of MXFP4 codes: sign * E2M1 magnitude * 2^exponent of the block."""
+    codes = np.asarray(codes)
+    mag = E2M1_MAGNITUDES[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    blocks = val.reshape(codes.shape[:-1] + (codes.shape[-1] // MX_BLOCK, MX_BLOCK))
+    out = blocks * np.ldexp(1.0, np.asarray(expo, dtype=np.int64))[..., None]
+    return out.reshape(codes.shape)
+
+
+def skim_values(x: np.ndarray) -> np.ndarray:
+    """What a skim pair sees of q or k: the MXFP4 round trip of each vector."""
+    return mxfp4_dequantize(*mxfp4_quantize(x))
+
+
+def tiered_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask_rows: np.ndarray,
+                          skim_rows: np.ndarray, scale: float):
+    """masked_attention_rows with per-pair tiers: where skim_rows [R, N] is
+    True the score is scale * (q^ . k^) of the MXFP4 round trips, elsewhere
+    scale * (q . k).  Softmax and P.V are unchanged."""
+    s = scale * np.where(skim_rows, skim_values(q) @ skim_values(k).T, q @ k.T)
+    s = np.where(mask_rows, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ v) / l, (m + np.log(l))[:, 0]
+
+
+def tiered_attention_head(q, k, v, keep: np.ndarray, skim: np.ndarray, tok_tile: np.ndarray,
+                          rows: np.ndarray, scale: float):
+    """Rows ``rows`` of one head with tile masks keep [nT, nT] and skim [nT, nT]
+    (skim only matters where keep is True)."""
+    tq = tok_tile[rows]
+    return tiered_attention_rows(q[rows], k, v, keep[tq][:, tok_tile], skim[tq][:, tok_tile], scale)
+
+
+def csr_tiers_to_tiles(row_ptr: np.ndarray, col_idx: np.ndarray, tier: np.ndarray, rows: int,
+                       nT: int) -> np.ndarray:
+    """Bool [rows, nT]: the skim flag of every kept (row, key tile) of a CSR
+    with one tier byte per entry (non-zero = skim)."""
+    out = np.zeros((rows, nT), dtype=bool)
+    for r in range(rows):
+        b, e = int(row_ptr[r]), int(row_ptr[r + 1])
+        out[r, col_idx[b:e]] = np.asarray(tier[b:e]) != 0
+    return out
 
 
 # ------------------------------------------------------------ split merging
