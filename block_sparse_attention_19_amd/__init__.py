@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         "vsa_tile_score_from_tokens": (ctypes.c_int, [SP, P, P, P]),
         "vsa_attn_workspace_bytes": (SZ, [SP, I32]),
         "vsa_attn_fwd": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, I32, P, SZ, P]),
+        "vsa_quantize_mxfp4": (ctypes.c_int, [SP, P, P, P, P]),
+        "vsa_attn_fwd_tiered": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                               P, P, I32, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -269,6 +272,74 @@ def attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: t
                               _ptr(col_idx), scale, _ptr(out), _ptr(lse), kv_chunk,
                               _ptr(workspace), workspace.numel(), _stream(dev)),
            "vsa_attn_fwd")
+    return out, lse
+
+
+def quantize_mxfp4(x_t: torch.Tensor, s: Shape, codes: Optional[torch.Tensor] = None,
+                   scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Token-major tiled bf16 q or k [B, heads, nT*64, D] -> MXFP4 (codes uint8
+    [B, heads, nT*64, D/2], E8M0 scales uint8 [B, heads, nT*64, D/32])."""
+    x_t = _require(x_t, torch.bfloat16, "x_t")
+    nT, D = num_tiles(s), s.head_dim
+    tok = (s.batch, s.heads, nT * 64, D)
+    if x_t.shape != tok:
+        raise ValueError("x_t shape does not match the shape")
+    dev = x_t.device
+    if codes is None:
+        codes = torch.empty(tok[:3] + (D // 2,), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(tok[:3] + (D // 32,), dtype=torch.uint8, device=dev)
+    if codes.numel() < x_t.numel() // 2 or scales.numel() < x_t.numel() // 32:
+        raise ValueError("codes / scales too small")
+    _check(lib().vsa_quantize_mxfp4(ctypes.byref(s), _ptr(x_t), _ptr(codes), _ptr(scales),
+                                    _stream(dev)), "vsa_quantize_mxfp4")
+    return codes, scales
+
+
+def attn_fwd_tiered(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
+                    q4: Tuple[torch.Tensor, torch.Tensor], k4: Tuple[torch.Tensor, torch.Tensor],
+                    row_ptr: torch.Tensor, col_idx: torch.Tensor, tier: torch.Tensor, s: Shape,
+                    scale: Optional[float] = None, kv_chunk: int = 0, with_lse: bool = True,
+                    out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """attn_fwd with a tier byte per CSR entry (non-zero = skim: the pair's
+    scores from the MXFP4 q4 / k4, each a (codes, scales) pair from
+    quantize_mxfp4).  `tier` must hold at least row_ptr[-1] bytes (not checked
+    here: that count lives on the device)."""
+    q_t = _require(q_t, torch.bfloat16, "q_t")
+    k_t = _require(k_t, torch.bfloat16, "k_t")
+    v_t = _require(v_t, torch.bfloat16, "v_t")
+    row_ptr = _require(row_ptr, torch.int32, "row_ptr")
+    col_idx = _require(col_idx, torch.int32, "col_idx")
+    tier = _require(tier, torch.uint8, "tier")
+    q4c, q4s = (_require(t, torch.uint8, "q4") for t in q4)
+    k4c, k4s = (_require(t, torch.uint8, "k4") for t in k4)
+    nT = num_tiles(s)
+    D = s.head_dim
+    tok = (s.batch, s.heads, nT * 64, D)
+    if q_t.shape != tok or k_t.shape != tok or v_t.shape != (s.batch, s.heads, nT, D, 64):
+        raise ValueError("q_t / k_t / v_t shapes do not match the shape")
+    for c, sc in ((q4c, q4s), (k4c, k4s)):
+        if c.numel() != q_t.numel() // 2 or sc.numel() != q_t.numel() // 32:
+            raise ValueError("MXFP4 codes / scales do not match the shape")
+    if row_ptr.numel() != s.batch * s.heads * nT + 1:
+        raise ValueError("row_ptr must have B*heads*nT + 1 entries")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q_t.device
+    if out is None:
+        out = torch.empty(tok, dtype=torch.bfloat16, device=dev)
+    lse = lse_out
+    if lse is None and with_lse:
+        lse = torch.empty(tok[:3], dtype=torch.float32, device=dev)
+    ws_bytes = attn_workspace_bytes(s, kv_chunk)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(lib().vsa_attn_fwd_tiered(ctypes.byref(s), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(q4c),
+                                     _ptr(q4s), _ptr(k4c), _ptr(k4s), _ptr(row_ptr),
+                                     _ptr(col_idx), _ptr(tier), scale, _ptr(out), _ptr(lse),
+                                     kv_chunk, _ptr(workspace), workspace.numel(), _stream(dev)),
+           "vsa_attn_fwd_tiered")
     return out, lse
 
 

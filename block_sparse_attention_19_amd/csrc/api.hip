@@ -289,4 +289,56 @@ vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t, co
                     "attention launch");
 }
 
+vsa_status vsa_quantize_mxfp4(const vsa_shape* s, const void* x_tiled, void* codes, void* scales,
+                              void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(x_tiled, 16, "x_tiled"));
+  VSA_TRY(check_ptr(codes, 16, "codes"));
+  VSA_TRY(check_ptr(scales, 16, "scales"));
+  return hip_status(launch_quantize_mxfp4(*s, x_tiled, codes, scales,
+                                          static_cast<hipStream_t>(stream)),
+                    "quantize launch");
+}
+
+vsa_status vsa_attn_fwd_tiered(const vsa_shape* s, const void* q_t, const void* k_t,
+                               const void* v_t, const void* q4, const void* q4_scales,
+                               const void* k4, const void* k4_scales, const int32_t* row_ptr,
+                               const int32_t* col_idx, const uint8_t* tier, float scale,
+                               void* o_t, float* lse_t, int32_t kv_chunk, void* ws,
+                               size_t ws_bytes, void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(q_t, 16, "q_t"));
+  VSA_TRY(check_ptr(k_t, 16, "k_t"));
+  VSA_TRY(check_ptr(v_t, 16, "v_t"));
+  VSA_TRY(check_ptr(q4, 16, "q4"));
+  VSA_TRY(check_ptr(q4_scales, 16, "q4_scales"));
+  VSA_TRY(check_ptr(k4, 16, "k4"));
+  VSA_TRY(check_ptr(k4_scales, 16, "k4_scales"));
+  VSA_TRY(check_ptr(row_ptr, 4, "row_ptr"));
+  VSA_TRY(check_ptr(col_idx, 4, "col_idx"));
+  VSA_TRY(check_ptr(tier, 1, "tier"));
+  VSA_TRY(check_ptr(o_t, 16, "o_t"));
+  if (lse_t) VSA_TRY(check_ptr(lse_t, 4, "lse_t"));
+  VSA_TRY(check_ptr(ws, 256, "ws"));
+  if (!(scale > 0.f) || scale > 3.0e38f) {
+    set_error("scale must be finite and > 0");
+    return VSA_ERR_INVALID_ARG;
+  }
+  if (kv_chunk < 0) {
+    set_error("kv_chunk must be >= 0");
+    return VSA_ERR_INVALID_ARG;
+  }
+  const size_t need = attn_layout(*s, kv_chunk).total;
+  if (ws_bytes < need) {
+    set_error("attention workspace %zu < %zu bytes", ws_bytes, need);
+    return VSA_ERR_CAPACITY;
+  }
+  int cus = 0;
+  VSA_TRY(device_cus(&cus));
+  const SkimInputs skim = {q4, q4_scales, k4, k4_scales, tier};
+  return hip_status(launch_attn(*s, q_t, k_t, v_t, row_ptr, col_idx, scale, o_t, lse_t, kv_chunk,
+                                ws, cus, static_cast<hipStream_t>(stream), &skim),
+                    "attention launch");
+}
+
 }  // extern "C"

@@ -43,6 +43,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte chunk (native vector)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kPlanThreads = 1024;
@@ -516,6 +518,12 @@ struct AttnArgs {
   const Unit* units;
   float* part_o;       // [slots][64][D]
   float* part_ml;      // [slots][2][64]
+  // skim tier (tiered instance only): MXFP4 Q and K, one tier byte per CSR entry
+  const uint8_t* q4;   // codes [BH][nT*64][D/2]
+  const uint8_t* q4s;  // E8M0 scales [BH][nT*64][D/32]
+  const uint8_t* k4;
+  const uint8_t* k4s;
+  const uint8_t* tier; // [nnz], 1 = skim
   int nT, nh, nw, T, H, W;
   float c2;            // scale * log2(e)
 };
@@ -541,6 +549,32 @@ struct Cfg {
   static constexpr int kDBlocks = D / 32;             // 32-row blocks of O^T
 };
 
+// MXFP4 K tiles of the skim tier: a row of D features is D/32 blocks of 16
+// code bytes (one 16-byte chunk each) plus D/32 E8M0 scale bytes.  In LDS a
+// tile (or half tile) is its codes, rows of D/2 bytes with swizzled chunks,
+// followed by its scales, rows of D/32 bytes.
+template <int D>
+struct Cfg4 {
+  static constexpr int kC4 = D / 32;                    // blocks (chunks) per row
+  static constexpr int kRowBytes = D / 2;
+  static constexpr int kTileCodes = kTileTokens * kRowBytes;
+  static constexpr int kTileAll = kTileCodes + kTileTokens * kC4;
+  static constexpr int kHalfCodes = 32 * kRowBytes;
+  static constexpr int kHalfAll = kHalfCodes + 32 * kC4;
+  static constexpr int kM = D / 64;                     // scaled MFMAs per 32-key half
+  static constexpr int kLdsBytes = 2 * kTileAll;        // beside the bf16 buffers
+  static_assert(4 * kHalfAll == kLdsBytes, "skim buffers");
+};
+
+// LDS byte offset of chunk c of MXFP4 K row `row`: the chunk index is XORed
+// with a row phase so that the 16 rows one read instruction touches per
+// 16-lane group land in distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k4_off(int row, int c) {
+  constexpr int C4 = Cfg4<D>::kC4;
+  return row * Cfg4<D>::kRowBytes + ((c ^ ((row / (16 / C4)) % C4)) << 4);
+}
+
 // LDS byte offset of 16-byte chunk c of K row `row` (swizzled).
 template <int D>
 __device__ __forceinline__ int k_off(int row, int c) {
@@ -563,6 +597,8 @@ struct WaveState {
   f32x16 o[Cfg<D>::kDBlocks];
   float m;  // running max (log2 domain, scaled)
   float l;  // this lane's partial sum of P
+  i32x4 q4[D / 64];  // skim tier: MXFP4 Q fragments (B operands)
+  int q4s;           // their scales, shifted so that byte 2m is fragment m's
 };
 
 // This wave's Q fragments (B operands of S^T = K Q^T): row q of its 32 query
@@ -571,6 +607,50 @@ template <int D>
 __device__ __forceinline__ void load_q(WaveState<D>& st, const uint16_t* qp) {
 #pragma unroll
   for (int t = 0; t < Cfg<D>::kKSteps; ++t) st.qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
+}
+
+// Skim tier.  This wave's MXFP4 Q fragments: for k-block m (64 features), the
+// 32-feature block 2m + h of query row q, and the row's scale word shifted so
+// that the scale of block 2m + h is its byte 2m.
+template <int D>
+__device__ __forceinline__ void load_q4(WaveState<D>& st, const uint8_t* q4row,
+                                        const uint8_t* q4srow, int h) {
+#pragma unroll
+  for (int m = 0; m < Cfg4<D>::kM; ++m)
+    st.q4[m] = *reinterpret_cast<const i32x4*>(q4row + (2 * m + h) * 16);
+  const uint32_t w = (D == 128) ? *reinterpret_cast<const uint32_t*>(q4srow)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(q4srow);
+  st.q4s = (int)(w >> (8 * h));
+}
+
+// One MXFP4 x MXFP4 product of K-block m: a 32x64 A (keys x features) and a
+// 64x32 B (features x queries), each lane holding one 32-feature block of one
+// row and that block's scale in byte OP of its scale word.
+template <int OP>
+__device__ __forceinline__ f32x16 mfma4(i32x4 a, i32x4 b, f32x16 c, int sa, int sb) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, OP, sa, OP, sb);
+}
+
+// S^T of 32 keys (rows r of an MXFP4 K buffer whose scales start at `sc`)
+// against this wave's queries, accumulated into s.
+template <int D>
+__device__ __forceinline__ f32x16 qk32_skim(const char* k4buf, const char* sc, int row,
+                                            const WaveState<D>& st, int h) {
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  const uint32_t w = (D == 128) ? *reinterpret_cast<const uint32_t*>(sc + row * 4)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(sc + row * 2);
+  const int ws = (int)(w >> (8 * h));
+  const i32x4 a0 = *reinterpret_cast<const i32x4*>(k4buf + k4_off<D>(row, h));
+  s = mfma4<0>(a0, st.q4[0], s, ws, st.q4s);
+  if constexpr (Cfg4<D>::kM > 1) {
+    const i32x4 a1 = *reinterpret_cast<const i32x4*>(k4buf + k4_off<D>(row, 2 + h));
+    s = mfma4<2>(a1, st.q4[1], s, ws, st.q4s);
+  }
+  return s;
 }
 
 // S^T (32 keys x 32 queries) = K Q^T for this wave's 32 query rows, from a
@@ -701,7 +781,7 @@ __device__ __forceinline__ uint32_t v_lane_off(int d0, int lane) {
 // workgroup (this is wave `w`).
 template <int D>
 __device__ __forceinline__ void dma_tile(char* buf, const char* ktile, const char* vtile, int w,
-                                         int nw, int lane) {
+                                         int nw, int lane, bool with_k = true) {
   constexpr int kBlocks = Cfg<D>::kTileBytes / 1024;
   constexpr int kPer = kBlocks / 4;
   constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
@@ -710,29 +790,90 @@ __device__ __forceinline__ void dma_tile(char* buf, const char* ktile, const cha
   for (int i = 0; i < kPer; ++i) {
     const int blk = w * kPer + i;  // rows blk*kRpb.. (K) / blk*8.. (V); the swizzle
                                    // phase depends on i only (w*kPer*kRpb % 16 == 0)
-    dma16(ktile + blk * 1024, k_lane_off<D>(i * kRpb, lane), buf + blk * 1024);
+    if (with_k) dma16(ktile + blk * 1024, k_lane_off<D>(i * kRpb, lane), buf + blk * 1024);
     dma16(vtile + blk * 1024, v_lane_off(i * 8, lane), buf + Cfg<D>::kTileBytes + blk * 1024);
   }
 }
 
+// Per-lane byte offset, within a 1 KB block of MXFP4 K codes, of the global
+// chunk that lands at LDS position 16*lane (the swizzle phase of k4_off only
+// depends on the row within the block).
+template <int D>
+__device__ __forceinline__ uint32_t k4_lane_off(int lane) {
+  constexpr int C4 = Cfg4<D>::kC4;
+  const int r = lane / C4;
+  return (uint32_t)(r * Cfg4<D>::kRowBytes + (((lane % C4) ^ ((r / (16 / C4)) % C4)) << 4));
+}
+
+// The MXFP4 K codes and scales of `rows` consecutive rows (64: a tile, 32: a
+// half), spread over `nwv` waves (this is wave `w` of them).
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_k4(char* buf, const char* codes, const char* scales, int w,
+                                       int nwv, int lane) {
+  constexpr int kBlocks = ROWS * Cfg4<D>::kRowBytes / 1024;
+  constexpr int kScaleDwords = ROWS * Cfg4<D>::kC4 / 4;  // scales move as dwords
+  for (int blk = w; blk < kBlocks; blk += nwv)
+    dma16(codes + blk * 1024, k4_lane_off<D>(lane), buf + blk * 1024);
+  if (w == nwv - 1 && lane < kScaleDwords)
+    __builtin_amdgcn_global_load_lds(scales + lane * 4, (VSA_LDS void*)(buf + ROWS * Cfg4<D>::kRowBytes),
+                                     4, 0, 0);
+}
+
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); }
+
+// Where a unit of the tiered instance finds its skim data: the MXFP4 K of its
+// (batch, head) and the tier bytes of its rows from its first key on (G
+// units: two rows, S units: t1 == t0).
+struct SkimRef {
+  const char* k4;
+  const char* k4s;
+  const uint8_t* t0;
+  const uint8_t* t1;
+};
+
+// Tier bits of entry i of a G unit: bit 0 first row skims, bit 1 second row.
+__device__ __forceinline__ int tier2(const SkimRef& sk, int i) {
+  return (sk.t0[i] != 0 ? 1 : 0) | (sk.t1[i] != 0 ? 2 : 0);
+}
 
 // One key tile of a G unit from LDS buffer CUR; the next tile is copied into
 // the other buffer by DMA while this one is computed on.  Both halves' score
 // MFMAs are issued before the first softmax so they run under its VALU work.
-template <int D, int CUR>
-__device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int code,
-                                       const char* kbase, const char* vbase, const AttnArgs& a,
-                                       int wave, int lane) {
+//
+// Tiered instance: `tc` / `tn` are the tier bits (tier2) of this tile and of
+// the next; the bf16 K of a tile is copied only if a row refines it and its
+// MXFP4 K (into the buffers past the bf16 ones) only if a row skims it.  V is
+// always bf16.  Each query tile's waves take the products of their own row's
+// tier.
+template <int D, int CUR, bool TIER>
+__device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int code, int tc,
+                                       int tn, const char* kbase, const char* vbase,
+                                       const SkimRef& sk, const AttnArgs& a, int wave, int lane,
+                                       int grp) {
   constexpr int TB = Cfg<D>::kTileBytes;
   const char* kbuf = smem + CUR * Cfg<D>::kSplitBytes;
   const char* vbuf = kbuf + TB;
-  if (jn >= 0)
+  if (jn >= 0) {
     dma_tile<D>(smem + (CUR ^ 1) * Cfg<D>::kSplitBytes, kbase + (int64_t)jn * TB,
-                vbase + (int64_t)jn * TB, wave, 4, lane);
+                vbase + (int64_t)jn * TB, wave, 4, lane, !TIER || tn != 3);
+    if constexpr (TIER) {
+      if (tn != 0)
+        dma_k4<D, 64>(smem + Cfg<D>::kLdsBytes + (CUR ^ 1) * Cfg4<D>::kTileAll,
+                      sk.k4 + (int64_t)jn * Cfg4<D>::kTileCodes,
+                      sk.k4s + (int64_t)jn * kTileTokens * Cfg4<D>::kC4, wave, 4, lane);
+    }
+  }
   const TileExtent ext = unpack_extent(code);
-  const f32x16 s0 = qk32<D>(kbuf, st, lane);
-  const f32x16 s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
+  f32x16 s0, s1;
+  if (TIER && ((tc >> grp) & 1)) {
+    const char* k4buf = smem + Cfg<D>::kLdsBytes + CUR * Cfg4<D>::kTileAll;
+    const int row = sigma(lane & 31), h = lane >> 5;
+    s0 = qk32_skim<D>(k4buf, k4buf + Cfg4<D>::kTileCodes, row, st, h);
+    s1 = qk32_skim<D>(k4buf, k4buf + Cfg4<D>::kTileCodes, 32 + row, st, h);
+  } else {
+    s0 = qk32<D>(kbuf, st, lane);
+    s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
+  }
   softmax_pv_half<D, false>(st, s0, vbuf, 0, lane, ext, a.c2);
   softmax_pv_half<D, false>(st, s1, vbuf, 1, lane, ext, a.c2);
   wait_dma();
@@ -744,31 +885,49 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int
 // streams into the other (a whole step to arrive, one barrier per step).
 // Column indices are read two tiles ahead and the next tile's extent one
 // tile ahead, so neither load is waited on.
-template <int D>
+template <int D, bool TIER>
 __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const int* cols,
                                             int nkeys, const char* kbase, const char* vbase,
-                                            const AttnArgs& a, int wave, int lane,
-                                            const uint16_t* qp) {
+                                            const SkimRef& sk, const AttnArgs& a, int wave,
+                                            int lane, const uint16_t* qp, int grp) {
   constexpr int TB = Cfg<D>::kTileBytes;
   const int j0 = uni(cols[0]);
   int jn = (1 < nkeys) ? uni(cols[1]) : -1;
   int code = uni(a.ext[j0]);
-  dma_tile<D>(smem, kbase + (int64_t)j0 * TB, vbase + (int64_t)j0 * TB, wave, 4, lane);
+  int tc = 0, tn = 0;  // tier bits of the current and the next tile (tiered instance)
+  if constexpr (TIER) {
+    tc = uni(tier2(sk, 0));
+    tn = (1 < nkeys) ? uni(tier2(sk, 1)) : 0;
+  }
+  dma_tile<D>(smem, kbase + (int64_t)j0 * TB, vbase + (int64_t)j0 * TB, wave, 4, lane,
+              !TIER || tc != 3);
+  if constexpr (TIER) {
+    if (tc != 0)
+      dma_k4<D, 64>(smem + Cfg<D>::kLdsBytes, sk.k4 + (int64_t)j0 * Cfg4<D>::kTileCodes,
+                    sk.k4s + (int64_t)j0 * kTileTokens * Cfg4<D>::kC4, wave, 4, lane);
+  }
   load_q<D>(st, qp);  // in flight with the first tile; one wait covers both
   wait_dma();
   lds_barrier();
   for (int step = 0; step < nkeys; step += 2) {
     int jnn_v = (step + 2 < nkeys) ? cols[step + 2] : -1;
     int cn_v = (jn >= 0) ? a.ext[jn] : 0;
-    g_step<D, 0>(st, smem, jn, code, kbase, vbase, a, wave, lane);
+    int tnn_v = 0;
+    if constexpr (TIER) tnn_v = (step + 2 < nkeys) ? tier2(sk, step + 2) : 0;
+    g_step<D, 0, TIER>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp);
     code = uni(cn_v);
     jn = uni(jnn_v);
+    tc = tn;
+    tn = uni(tnn_v);
     if (step + 1 >= nkeys) break;
     jnn_v = (step + 3 < nkeys) ? cols[step + 3] : -1;
     cn_v = (jn >= 0) ? a.ext[jn] : 0;
-    g_step<D, 1>(st, smem, jn, code, kbase, vbase, a, wave, lane);
+    if constexpr (TIER) tnn_v = (step + 3 < nkeys) ? tier2(sk, step + 3) : 0;
+    g_step<D, 1, TIER>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp);
     code = uni(cn_v);
     jn = uni(jnn_v);
+    tc = tn;
+    tn = uni(tnn_v);
   }
 }
 
@@ -777,7 +936,7 @@ __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const 
 // split sharing the blocks (this is wave `wi` of them).
 template <int D>
 __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const char* vtile, int kb,
-                                         int wi, int nwv, int lane) {
+                                         int wi, int nwv, int lane, bool with_k = true) {
   constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
   constexpr int KH = 32 * Cfg<D>::kRowBytes;   // bytes of a K half
   constexpr int kKBlocks = KH / 1024, kVBlocks = D * 64 / 1024;
@@ -785,8 +944,9 @@ __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const cha
 #pragma unroll
   for (int i = 0; i < kKBlocks / 2; ++i) {
     const int blk = wi * (kKBlocks / 2) + i;   // swizzle phase depends on i only
-    dma16(ktile + (32 * kb) * Cfg<D>::kRowBytes + blk * 1024, k_lane_off<D>(i * kRpb, lane),
-          buf + blk * 1024);
+    if (with_k)
+      dma16(ktile + (32 * kb) * Cfg<D>::kRowBytes + blk * 1024, k_lane_off<D>(i * kRpb, lane),
+            buf + blk * 1024);
   }
 #pragma unroll
   for (int i = 0; i < kVBlocks / 2; ++i) {
@@ -803,23 +963,51 @@ __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const cha
 // S units: one query tile; waves 0-1 (rows 0-31, 32-63) take the key tiles at
 // even positions of the list and waves 2-3 the odd ones.  Each key split
 // double-buffers half tiles (32 keys of K and of V^T) in its own LDS region,
-// so the two tiles a step needs fit beside their prefetches.
-template <int D>
+// so the two tiles a step needs fit beside their prefetches.  Tiered
+// instance: a skim tile brings its MXFP4 K half instead of the bf16 one, into
+// the split's half buffers past the bf16 region.
+template <int D, bool TIER>
 __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const int* cols,
                                             int nkeys, const char* kbase, const char* vbase,
-                                            const AttnArgs& a, int wave, int lane, int grp,
-                                            const uint16_t* qp) {
+                                            const SkimRef& sk, const AttnArgs& a, int wave,
+                                            int lane, int grp, const uint16_t* qp) {
   constexpr int TB = Cfg<D>::kTileBytes;
   constexpr int KH = 32 * Cfg<D>::kRowBytes;
   constexpr int BUF = KH + D * 64;                       // one half-tile buffer
+  constexpr int H4 = Cfg4<D>::kHalfAll;                  // one MXFP4 K half buffer
   static_assert(4 * BUF <= Cfg<D>::kLdsBytes, "S unit buffers");
   char* region = smem + grp * 2 * BUF;
+  char* region4 = smem + Cfg<D>::kLdsBytes + grp * 2 * H4;
   const int wi = wave & 1;
   const int nsteps = (nkeys + 1) / 2;
+  const int krow = sigma(lane & 31), h = lane >> 5;
   int j = (grp < nkeys) ? uni(cols[grp]) : -1;
   int jn = (2 + grp < nkeys) ? uni(cols[2 + grp]) : -1;
   int code = (j >= 0) ? uni(a.ext[j]) : 0;
-  if (j >= 0) dma_half<D>(region, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, 0, wi, 2, lane);
+  int t = 0, tn = 0;  // this split's current / next tile skims (tiered instance)
+  if constexpr (TIER) {
+    t = (j >= 0) ? uni(sk.t0[grp] != 0 ? 1 : 0) : 0;
+    tn = (jn >= 0) ? uni(sk.t0[2 + grp] != 0 ? 1 : 0) : 0;
+  }
+  // half kb of tile jj (skim flag tt) into LDS half buffer `which`
+  auto fetch = [&](int jj, int tt, int kb, int which) {
+    dma_half<D>(region + which * BUF, kbase + (int64_t)jj * TB, vbase + (int64_t)jj * TB, kb, wi,
+                2, lane, !TIER || !tt);
+    if constexpr (TIER) {
+      if (tt)
+        dma_k4<D, 32>(region4 + which * H4,
+                      sk.k4 + (int64_t)jj * Cfg4<D>::kTileCodes + kb * Cfg4<D>::kHalfCodes,
+                      sk.k4s + ((int64_t)jj * kTileTokens + 32 * kb) * Cfg4<D>::kC4, wi, 2, lane);
+    }
+  };
+  auto scores = [&](int tt, int which) -> f32x16 {
+    if (TIER && tt) {
+      const char* b4 = region4 + which * H4;
+      return qk32_skim<D>(b4, b4 + Cfg4<D>::kHalfCodes, krow, st, h);
+    }
+    return qk32<D>(region + which * BUF, st, lane);
+  };
+  if (j >= 0) fetch(j, t, 0, 0);
   load_q<D>(st, qp);  // in flight with the first half tile; one wait covers both
   wait_dma();
   lds_barrier();
@@ -827,18 +1015,19 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     const int pnn = 2 * (i + 2) + grp;
     const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;
     const int cn_v = (jn >= 0) ? a.ext[jn] : 0;
+    int tnn_v = 0;
+    if constexpr (TIER) tnn_v = (pnn < nkeys) ? (sk.t0[pnn] != 0 ? 1 : 0) : 0;
     const TileExtent ext = unpack_extent(code);
     if (j >= 0) {
-      dma_half<D>(region + BUF, kbase + (int64_t)j * TB, vbase + (int64_t)j * TB, 1, wi, 2, lane);
-      const f32x16 s0 = qk32<D>(region, st, lane);
+      fetch(j, t, 1, 1);
+      const f32x16 s0 = scores(t, 0);
       softmax_pv_half<D, true>(st, s0, region + KH, 0, lane, ext, a.c2);
     }
     wait_dma();
     lds_barrier();
-    if (jn >= 0)
-      dma_half<D>(region, kbase + (int64_t)jn * TB, vbase + (int64_t)jn * TB, 0, wi, 2, lane);
+    if (jn >= 0) fetch(jn, tn, 0, 0);
     if (j >= 0) {
-      const f32x16 s1 = qk32<D>(region + BUF, st, lane);
+      const f32x16 s1 = scores(t, 1);
       softmax_pv_half<D, true>(st, s1, region + BUF + KH, 1, lane, ext, a.c2);
     }
     wait_dma();
@@ -846,10 +1035,12 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     j = jn;
     code = uni(cn_v);
     jn = uni(jnn_v);
+    t = tn;
+    tn = uni(tnn_v);
   }
 }
 
-template <int D>
+template <int D, bool TIER>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_unit;
@@ -922,10 +1113,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     const int nkeys = u.ke - u.kb;
     const char* kbase = reinterpret_cast<const char*>(args.k) + bh * (int64_t)nT * TC * 16;
     const char* vbase = reinterpret_cast<const char*>(args.v) + bh * (int64_t)nT * TC * 16;
+    SkimRef sk = {nullptr, nullptr, nullptr, nullptr};
+    if constexpr (TIER) {
+      const int64_t tiles_before = bh * (int64_t)nT * kTileTokens;  // rows of earlier heads
+      sk.k4 = reinterpret_cast<const char*>(args.k4) + tiles_before * Cfg4<D>::kRowBytes;
+      sk.k4s = reinterpret_cast<const char*>(args.k4s) + tiles_before * Cfg4<D>::kC4;
+      sk.t0 = args.tier + uni(args.row_ptr[u.row[0]]) + u.kb;
+      sk.t1 = g_mode ? args.tier + uni(args.row_ptr[u.row[1]]) + u.kb : sk.t0;
+      load_q4<D>(st, args.q4 + (qrow0 + q) * Cfg4<D>::kRowBytes,
+                 args.q4s + (qrow0 + q) * Cfg4<D>::kC4, h);
+    }
     if (g_mode)
-      run_steps_g<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane, qp);
+      run_steps_g<D, TIER>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, qp, grp);
     else
-      run_steps_s<D>(st, smem, cols, nkeys, kbase, vbase, args, wave, lane, grp, qp);
+      run_steps_s<D, TIER>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, grp, qp);
 
     // S units: merge the two key splits (waves 2,3 -> waves 0,1) through LDS.
     if (!g_mode) {
@@ -1037,7 +1238,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const Header* hdr, const C
 
 hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const void* v,
                        const int* row_ptr, const int* col_idx, float scale, void* o, float* lse,
-                       int kv_chunk, void* ws, int cus, hipStream_t stream) {
+                       int kv_chunk, void* ws, int cus, hipStream_t stream, const SkimInputs* skim) {
   const Grid g = make_grid(s);
   const AttnLayout L = attn_layout(s, kv_chunk);
   char* w = static_cast<char*>(ws);
@@ -1085,25 +1286,40 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   aa.H = s.H;
   aa.W = s.W;
   aa.c2 = scale * kLog2e;
+  aa.q4 = skim ? static_cast<const uint8_t*>(skim->q4) : nullptr;
+  aa.q4s = skim ? static_cast<const uint8_t*>(skim->q4_scales) : nullptr;
+  aa.k4 = skim ? static_cast<const uint8_t*>(skim->k4) : nullptr;
+  aa.k4s = skim ? static_cast<const uint8_t*>(skim->k4_scales) : nullptr;
+  aa.tier = skim ? skim->tier : nullptr;
   const int grid = (int)std::min<int64_t>(L.max_units, 2LL * cus);
   if (s.head_dim == 128) {
-    const size_t lds = Cfg<128>::kLdsBytes;
-    attn_kernel<128><<<grid, kThreads, lds, stream>>>(aa);
+    if (skim)
+      attn_kernel<128, true><<<grid, kThreads, Cfg<128>::kLdsBytes + Cfg4<128>::kLdsBytes, stream>>>(aa);
+    else
+      attn_kernel<128, false><<<grid, kThreads, Cfg<128>::kLdsBytes, stream>>>(aa);
     combine_kernel<128><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
   } else {
-    const size_t lds = Cfg<64>::kLdsBytes;
-    attn_kernel<64><<<grid, kThreads, lds, stream>>>(aa);
+    if (skim)
+      attn_kernel<64, true><<<grid, kThreads, Cfg<64>::kLdsBytes + Cfg4<64>::kLdsBytes, stream>>>(aa);
+    else
+      attn_kernel<64, false><<<grid, kThreads, Cfg<64>::kLdsBytes, stream>>>(aa);
     combine_kernel<64><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
   }
   return hipGetLastError();
 }
 
 hipError_t attn_set_lds_limits() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<128>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<128>::kLdsBytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<64>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<64>::kLdsBytes);
+  const void* fns[4] = {reinterpret_cast<const void*>(attn_kernel<128, false>),
+                        reinterpret_cast<const void*>(attn_kernel<128, true>),
+                        reinterpret_cast<const void*>(attn_kernel<64, false>),
+                        reinterpret_cast<const void*>(attn_kernel<64, true>)};
+  const int lds[4] = {Cfg<128>::kLdsBytes, Cfg<128>::kLdsBytes + Cfg4<128>::kLdsBytes,
+                      Cfg<64>::kLdsBytes, Cfg<64>::kLdsBytes + Cfg4<64>::kLdsBytes};
+  for (int i = 0; i < 4; ++i) {
+    const hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace vsa

@@ -65,9 +65,20 @@ hipError_t launch_build_mask(const vsa_shape& s, const uint8_t* radii, const flo
                              int dense_count, int r_max, int* row_ptr, int* col_idx,
                              uint8_t* routed, void* ws, hipStream_t stream);
 AttnLayout attn_layout(const vsa_shape& s, int kv_chunk);
+// Inputs of the skim tier (MXFP4 Q and K, one tier byte per CSR entry).
+struct SkimInputs {
+  const void* q4;
+  const void* q4_scales;
+  const void* k4;
+  const void* k4_scales;
+  const uint8_t* tier;
+};
 hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const void* v,
                        const int* row_ptr, const int* col_idx, float scale, void* o, float* lse,
-                       int kv_chunk, void* ws, int cus, hipStream_t stream);
+                       int kv_chunk, void* ws, int cus, hipStream_t stream,
+                       const SkimInputs* skim = nullptr);
+hipError_t launch_quantize_mxfp4(const vsa_shape& s, const void* x_tiled, void* codes,
+                                 void* scales, hipStream_t stream);
 hipError_t attn_set_lds_limits();
 
 void set_error(const char* fmt, ...);

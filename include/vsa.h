@@ -214,6 +214,53 @@ vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t,
                         float scale, void* o_t, float* lse_t, int32_t kv_chunk,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* ----------------------------------------------------- low-precision tier
+ * "Triage: Skip, Skim, or Refine Attention Tiles in Video Diffusion
+ * Transformers" (plain-words summary; "Route by estimated error"): every
+ * attention tile is skipped, computed in a quick 4-bit version ("skim") or
+ * computed accurately ("refine").  The pages give neither the 4-bit format
+ * nor the router's formulas, so here the tier of every kept (query tile, key
+ * tile) pair is an input and the format is OCP MXFP4 (E2M1 elements, one E8M0
+ * power-of-two scale per 32 consecutive features), which gfx950's scaled MFMA
+ * consumes.  Skipped tiles are the ones absent from the CSR.
+ *
+ * vsa_quantize_mxfp4: MXFP4 encoding of a token-major tiled Q or K along D,
+ * per the OCP Microscaling Formats specification v1.0: block scale
+ * X = 2^(floor(log2 max|v|) - 2) (exponent clamped to [-127, 127]; -127 for an
+ * all-zero block), each v / X rounded to the nearest of +-{0, .5, 1, 1.5, 2,
+ * 3, 4, 6} with ties to the even code and saturation at 6; the sign of -0.0
+ * is kept.
+ *   x_tiled  bf16 [B][heads][nT*64][D] (VSA_LAYOUT_TOKEN_MAJOR), finite.
+ *   codes    uint8 [B][heads][nT*64][D/2]: element 2i in the low nibble of
+ *            byte i, element 2i+1 in the high nibble; a nibble is sign (bit 3)
+ *            and the index (bits 0-2) into {0, .5, 1, 1.5, 2, 3, 4, 6}.
+ *   scales   uint8 [B][heads][nT*64][D/32]: E8M0, exponent + 127.
+ * All buffers are the caller's; codes/scales are fully written.
+ * Errors: INVALID_ARG (shape, NULL or misaligned pointer: 16 bytes for all
+ * three), UNSUPPORTED (head_dim not 64/128), OVERFLOW.
+ */
+vsa_status vsa_quantize_mxfp4(const vsa_shape* s, const void* x_tiled, void* codes, void* scales,
+                              void* stream);
+
+/* vsa_attn_fwd_tiered: vsa_attn_fwd with a tier per CSR entry.  Where
+ * tier[e] != 0 the scores of that (query tile, key tile) pair are computed
+ * from the MXFP4 Q and K (products of the dequantised values, fp32
+ * accumulation); elsewhere from the bf16 Q and K.  Softmax, P.V (bf16 P and V)
+ * and the output are as in vsa_attn_fwd; one softmax spans both tiers.
+ *   q_t, k_t, v_t, row_ptr, col_idx, scale, o_t, lse_t, kv_chunk, ws,
+ *   ws_bytes: as vsa_attn_fwd (the same workspace size).
+ *   q4, q4_scales, k4, k4_scales: vsa_quantize_mxfp4 of q_t and k_t.
+ *   tier     uint8 [nnz], one per CSR entry (same order as col_idx).
+ * Errors: as vsa_attn_fwd, plus INVALID_ARG for NULL or misaligned MXFP4
+ * buffers (16 bytes) or a NULL tier.
+ */
+vsa_status vsa_attn_fwd_tiered(const vsa_shape* s, const void* q_t, const void* k_t,
+                               const void* v_t, const void* q4, const void* q4_scales,
+                               const void* k4, const void* k4_scales, const int32_t* row_ptr,
+                               const int32_t* col_idx, const uint8_t* tier, float scale,
+                               void* o_t, float* lse_t, int32_t kv_chunk, void* ws,
+                               size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

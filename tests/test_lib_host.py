@@ -134,3 +134,31 @@ def test_token_calls_validate_before_launch():
     assert L.vsa_tile_score_from_tokens(None, good, good, None) == INVALID
     s96 = vsa.shape(1, 2, 96, 8, 16, 16)
     assert L.vsa_tile_radius_from_tokens(ctypes.byref(s96), good, good, None) == UNSUPPORTED
+
+
+def test_skim_calls_validate_before_launch():
+    L = vsa.lib()
+    s = vsa.shape(1, 2, 64, 8, 16, 16)
+    sp = ctypes.byref(s)
+    good = _p(0x10000)
+    assert L.vsa_quantize_mxfp4(sp, None, good, good, None) == INVALID
+    assert L.vsa_quantize_mxfp4(sp, good, _p(0x10008), good, None) == INVALID
+    assert L.vsa_quantize_mxfp4(sp, good, good, None, None) == INVALID
+    s96 = vsa.shape(1, 2, 96, 8, 16, 16)
+    assert L.vsa_quantize_mxfp4(ctypes.byref(s96), good, good, good, None) == UNSUPPORTED
+    ws = vsa.attn_workspace_bytes(s, 0)
+
+    def call(**kw):
+        a = dict(q=good, k=good, v=good, q4=good, q4s=good, k4=good, k4s=good, rp=good, ci=good,
+                 tier=good, scale=0.125, o=good, lse=None, chunk=0, ws=good, wsb=ws)
+        a.update(kw)
+        return L.vsa_attn_fwd_tiered(sp, a["q"], a["k"], a["v"], a["q4"], a["q4s"], a["k4"],
+                                     a["k4s"], a["rp"], a["ci"], a["tier"], a["scale"], a["o"],
+                                     a["lse"], a["chunk"], a["ws"], a["wsb"], None)
+    assert call(tier=None) == INVALID
+    assert call(q4=None) == INVALID
+    assert call(k4s=_p(0x10004)) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(chunk=-1) == INVALID
+    assert call(wsb=ws - 1) == CAPACITY
+    assert vsa.lib().vsa_last_error().decode()

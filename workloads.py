@@ -173,6 +173,15 @@ def token_inputs(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
     return np.ascontiguousarray(b), np.ascontiguousarray(s)
 
 
+# Tiers of the low-precision "skim" path: one byte per kept (query tile, key
+# tile) pair in CSR order, 1 (skim) with probability p_skim, drawn i.i.d. by
+# stream 8.  The pages' router (estimated error per tile) has no formulas, so
+# a fixed skim fraction stands in for it.
+def tiers(w: Workload, nnz: int, p_skim: float = 0.5) -> np.ndarray:
+    """uint8 [nnz]: 1 = skim, 0 = refine."""
+    return (_rng(w, 8, 0).random(nnz) < p_skim).astype(np.uint8)
+
+
 def qkv(w: Workload, heads: Optional[range] = None):
     """Q, K, V as bf16 bit patterns, each [B=1, N, heads, D] (uint16)."""
     hs = range(w.heads) if heads is None else heads
