@@ -12,7 +12,9 @@ step (kept tile pairs x 4*64*64*D flops over the step time); ``roofline``
 rates the attention kernel alone against the bf16 MFMA peak; ``cpu_baseline``
 times the fp64 CPU oracle on a bounded sample of the same workload;
 ``token_level_calls`` times the per-token -> per-tile calls (budget -> radius,
-tile radius, tile score) at the workload's size, outside the step.
+tile radius, tile score) and ``skim_tier`` the MXFP4 encoding and the tiered
+attention call (half / all kept pairs skimmed) at the workload's size, both
+outside the step.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 1]
 """
@@ -136,6 +138,56 @@ def token_level_calls(w, sh, dev, stream, reps):
     return out
 
 
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 MFMA (the skim tier's score products)
+
+
+def skim_tier(w, sh, dev, stream, reps, q_t, k_t, v_t, rp, ci, nnz, ws, o_t, attn_ms, kv_chunk):
+    """The low-precision tier at the workload's size, outside the step: the
+    MXFP4 encoding of Q and K, and the tiered attention call with half and with
+    all kept pairs skimmed (tiers drawn i.i.d.).  Its bound mixes two peaks:
+    a skim pair's Q.K^T (2*64*64*D flops) at the FP4 rate, everything else
+    (its P.V, both products of a refine pair) at the bf16 rate."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_19_amd as vsa
+    import workloads as wl
+    rows = q_t.shape[2] * w.heads
+    q4 = (torch.empty(q_t.shape[:3] + (w.D // 2,), dtype=torch.uint8, device=dev),
+          torch.empty(q_t.shape[:3] + (w.D // 32,), dtype=torch.uint8, device=dev))
+    k4 = (torch.empty_like(q4[0]), torch.empty_like(q4[1]))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    q_ms = timed(lambda: (vsa.quantize_mxfp4(q_t, sh, *q4), vsa.quantize_mxfp4(k_t, sh, *k4)))
+    moved = 2 * rows * (w.D * 2 + w.D // 2 + w.D // 32)
+    out = {"quantize_qk": {"us": round(q_ms * 1e3, 2), "hbm_bytes": int(moved),
+                           "GB/s": round(moved / (q_ms * 1e-3) / 1e9, 1)}}
+    pair = 2.0 * 64 * 64 * w.D  # flops of one product of one kept pair
+    for p_skim in (0.5, 1.0):
+        tier = torch.from_numpy(wl.tiers(w, nnz, p_skim)).to(dev)
+        n_skim = int(tier.sum().item())
+        ms = timed(lambda: vsa.attn_fwd_tiered(q_t, k_t, v_t, q4, k4, rp, ci, tier, sh, w.scale,
+                                               kv_chunk, out=o_t, workspace=ws, with_lse=False))
+        bound_ms = ((2 * nnz - n_skim) * pair / (PEAK_BF16_TFLOPS * 1e12) +
+                    n_skim * pair / (PEAK_FP4_TFLOPS * 1e12)) * 1e3
+        out[f"attn_tiered_p{p_skim}"] = {
+            "skim_pairs": n_skim, "ms": round(ms, 4),
+            "TFLOP/s": round(2 * nnz * pair / (ms * 1e-3) / 1e12, 2),
+            "mixed_peak_ms": round(bound_ms, 4), "frac": round(bound_ms / ms, 4),
+            "speedup_vs_bf16_call": round(attn_ms / ms, 3)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -242,6 +294,8 @@ def main():
         "attn_valid_token_tflops": round(valid_flops / (attn_ms * 1e-3) / 1e12, 2),
     }
     line["token_level_calls"] = token_level_calls(w, sh, dev, stream, args.steps)
+    line["skim_tier"] = skim_tier(w, sh, dev, stream, args.steps, q_t, k_t, v_t, mbuf[0], mbuf[1],
+                                  nnz, ws, o_t, attn_ms, args.kv_chunk)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, r, s, kcount, args.cpu_seconds)
     else:
