@@ -258,3 +258,75 @@ def test_attention_d64_medium_split(kv_chunk):
     out = _run_all(w, q, k, v, r, s, kcount, kv_chunk=kv_chunk)
     ref, _ = vo.attention(q, k, v, r, s, kcount, T, H, W, w.scale)
     assert_close(f64_of(out["o"]), ref, f"O D=64 kv_chunk={kv_chunk}")
+
+
+def _random_csr(rng, rows, nT):
+    """Any CSR the call accepts: empty rows, single columns, complete rows
+    (which run as G units) and random ascending column subsets."""
+    lens = []
+    cols = []
+    for _ in range(rows):
+        u = rng.random()
+        n = 0 if u < 0.1 else 1 if u < 0.2 else nT if u < 0.35 else int(rng.integers(2, nT))
+        lens.append(n)
+        cols.append(np.sort(rng.choice(nT, n, replace=False)))
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return rp, np.concatenate(cols).astype(np.int32)
+
+
+def _check_csr_attention(w, q, k, v, rp, ci, o, lse, skim=None):
+    """O / LSE of an arbitrary CSR against the oracle; rows without keys must
+    give zeros and LSE = -inf."""
+    nT = w.n_cells
+    tt = vo.token_tile(w.T, w.H, w.W)
+    got = f64_of(o)[0]
+    lse_t = lse.cpu().numpy().astype(np.float64)[0]
+    g_all, r_all = [], []
+    for h in range(w.heads):
+        keep = np.zeros((nT, nT), bool)
+        for a in range(nT):
+            row = h * nT + a
+            keep[a, ci[rp[row]:rp[row + 1]]] = True
+        nonempty = keep.any(axis=1)
+        rows = np.flatnonzero(nonempty[tt])
+        empty = np.flatnonzero(~nonempty[tt])
+        qf, kf, vf = (vo.bf16_to_f64(x[0, :, h]) for x in (q, k, v))
+        if skim is None:
+            ref, lref = vo.attention_head_rows(qf, kf, vf, keep, tt, rows, w.scale)
+        else:
+            ref, lref = vo.tiered_attention_head(qf, kf, vf, keep, skim[h], tt, rows, w.scale)
+        g_all.append(got[rows, h])
+        r_all.append(ref)
+        assert np.all(got[empty, h] == 0.0), "rows without keys must be zero"
+        # LSE in token-major order: token n of tile tau sits at slot tau*64 + local index
+        slot = vo.permute(np.arange(w.tokens, dtype=np.float64)[None, :, None, None], w.T, w.H, w.W)[0, 0, :, 0]
+        valid = vo.permute(np.ones((1, w.tokens, 1, 1)), w.T, w.H, w.W)[0, 0, :, 0] > 0
+        tok_of_slot = np.full(slot.shape, -1, np.int64)
+        tok_of_slot[valid] = slot[valid].astype(np.int64)
+        pos = np.full(w.tokens, -1, np.int64)
+        pos[tok_of_slot[valid]] = np.flatnonzero(valid)
+        assert np.abs(lse_t[h, pos[rows]] - lref).max() <= LSE_ABS
+        if len(empty):
+            assert np.all(np.isneginf(lse_t[h, pos[empty]]))
+    assert_close(np.concatenate(g_all), np.concatenate(r_all), "O arbitrary CSR")
+
+
+@pytest.mark.parametrize("D,kv_chunk", [(64, 0), (128, 0), (128, 3)])
+def test_attention_arbitrary_csr(D, kv_chunk):
+    """Any CSR, not only the mask builder's: empty rows, one-column rows,
+    complete rows (G units) and random column subsets."""
+    T, H, W, heads = 9, 10, 11, 2
+    w = wl.custom(T, H, W, heads, D, radius_set=(1,), cid=413)
+    q, k, v = wl.qkv(w)
+    nT = w.n_cells
+    rp, ci = _random_csr(np.random.default_rng(D + kv_chunk), heads * nT, nT)
+    say(f"attention arbitrary CSR D={D} kv_chunk={kv_chunk} nnz={rp[-1]}")
+    sh = _shape(w)
+    q_t = vsa.tile_permute(bf16_to_dev(q), sh, vsa.LAYOUT_TOKEN_MAJOR)
+    k_t = vsa.tile_permute(bf16_to_dev(k), sh, vsa.LAYOUT_TOKEN_MAJOR)
+    v_t = vsa.tile_permute(bf16_to_dev(v), sh, vsa.LAYOUT_FEATURE_MAJOR)
+    o_t, lse = vsa.attn_fwd(q_t, k_t, v_t, torch.from_numpy(rp).to(dev()),
+                            torch.from_numpy(ci).to(dev()), sh, w.scale, kv_chunk)
+    o = vsa.tile_unpermute(o_t, sh)
+    torch.cuda.synchronize()
+    _check_csr_attention(w, q, k, v, rp, ci, o, lse)

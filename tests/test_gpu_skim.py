@@ -242,3 +242,24 @@ def test_attention_tiered_wan13b_sampled():
         g_all.append(got[rows, h])
         r_all.append(O[0])
     assert_close(np.concatenate(g_all), np.concatenate(r_all), f"{w.name} tiered sampled")
+
+
+def test_attention_tiered_arbitrary_csr():
+    """The tiered call on any CSR (empty rows, one-column rows, complete rows
+    as G units, random subsets) with random tiers."""
+    from test_gpu_parity import _check_csr_attention, _random_csr
+    T, H, W, heads, D = 9, 10, 11, 2, 128
+    w = wl.custom(T, H, W, heads, D, radius_set=(1,), cid=423)
+    q, k, v = wl.qkv(w)
+    nT = w.n_cells
+    rp, ci = _random_csr(np.random.default_rng(9), heads * nT, nT)
+    tier = wl.tiers(w, int(rp[-1]), 0.5)
+    say(f"tiered arbitrary CSR nnz={rp[-1]}")
+    sh = _shape(w)
+    q_t = vsa.tile_permute(bf16_to_dev(q), sh, vsa.LAYOUT_TOKEN_MAJOR)
+    k_t = vsa.tile_permute(bf16_to_dev(k), sh, vsa.LAYOUT_TOKEN_MAJOR)
+    v_t = vsa.tile_permute(bf16_to_dev(v), sh, vsa.LAYOUT_FEATURE_MAJOR)
+    o, _, lse = _tiered(w, sh, q_t, k_t, v_t, torch.from_numpy(rp).to(dev()),
+                        torch.from_numpy(ci).to(dev()), tier)
+    skim = vo.csr_tiers_to_tiles(rp, ci, tier, heads * nT, nT).reshape(heads, nT, nT)
+    _check_csr_attention(w, q, k, v, rp, ci, o, lse, skim=skim)
