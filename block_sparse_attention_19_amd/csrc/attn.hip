@@ -707,12 +707,16 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
       s[r] = ok ? s[r] : -INFINITY;
     }
   }
+  // This lane's 16 scores decide whether the running max must move: the
+  // query's max over both lane halves exceeds m + slack exactly when one
+  // half's does, so the halves are combined (a cross-lane swap, which does
+  // not overlap the other wave's MFMAs) only in the rare rescale branch, and
+  // m stays the same in both halves.
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = max_halves(mx);
-  const float mc = mx * c2;
-  if (__any(mc > st.m + kRescaleSlack)) {
+  if (__any(mx * c2 > st.m + kRescaleSlack)) {
+    const float mc = max_halves(mx) * c2;
     const float mn = fmaxf(st.m, mc);
     const float alpha = (mn == -INFINITY) ? 1.f : exp2f(st.m - mn);
     st.l *= alpha;
@@ -725,19 +729,19 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
   // every tile holds at least one valid key, so the running max is finite here
   const float mneg = -st.m;
   bf16x8 pb[2];
+  float pf[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], c2, mneg));
-  // Row sum of the bf16 probabilities that P.V multiplies (one v_dot2 per pair:
-  // numerator and denominator use the same rounded weights).
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float lsum = st.l;
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    const bf16x2 pair = {pb[r >> 3][r & 7], pb[r >> 3][(r & 7) + 1]};
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
+  for (int r = 0; r < 16; ++r) {
+    pf[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, mneg));
+    pb[r >> 3][r & 7] = (__bf16)pf[r];
   }
-  st.l = lsum;
+  // Row sum of the fp32 probabilities by a pairwise tree of plain adds (these
+  // overlap the other wave's MFMAs; bf16 dot products do not).  P.V takes the
+  // round-to-nearest bf16 P, whose rounding errors are unbiased, so numerator
+  // and denominator agree to well within the bf16 tolerance.
+  const float a0 = pf[0] + pf[1], a1 = pf[2] + pf[3], a2 = pf[4] + pf[5], a3 = pf[6] + pf[7];
+  const float a4 = pf[8] + pf[9], a5 = pf[10] + pf[11], a6 = pf[12] + pf[13], a7 = pf[14] + pf[15];
+  st.l += ((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7));
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
