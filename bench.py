@@ -16,7 +16,7 @@ tile radius, tile score) and ``skim_tier`` the MXFP4 encoding and the tiered
 attention call (half / all kept pairs skimmed) at the workload's size, both
 outside the step.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 1]
+    python bench.py [--gpus 1] [--steps 30] [--warmup 30] [--workload 1]
 """
 from __future__ import annotations
 
@@ -40,8 +40,10 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_19_amd", "csrc", "attn.hip
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    # the clock settles over the first few dozen launches of the call (per-call
+    # time falls by ~10% over the first ~25), so the default warm-up is long
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--dense-index", type=int, default=0,
                     help="which routed count of the workload's sweep")
