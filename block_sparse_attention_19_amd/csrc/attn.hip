@@ -781,21 +781,36 @@ __device__ __forceinline__ uint32_t v_lane_off(int d0, int lane) {
   return (uint32_t)((lane >> 3) * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4));
 }
 
+// The same copy through a buffer resource over one tile: the descriptor is
+// built from the tile's (uniform) base in scalar registers, the uniform part of
+// the source offset is the scalar offset and the per-lane part a loop-invariant
+// VGPR, so issuing a copy takes no vector arithmetic (the pointer form needs
+// 64-bit vector adds per copy).  Reads past the tile's bytes would return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t soff,
+                                       char* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (VSA_LDS void*)lds_block, 16, lane_off, soff, 0, 0);
+}
+
 // All blocks of one K tile and one V^T tile, spread over the 4 waves of the
 // workgroup (this is wave `w`).
 template <int D>
 __device__ __forceinline__ void dma_tile(char* buf, const char* ktile, const char* vtile, int w,
                                          int nw, int lane, bool with_k = true) {
-  constexpr int kBlocks = Cfg<D>::kTileBytes / 1024;
+  constexpr int TB = Cfg<D>::kTileBytes;
+  constexpr int kBlocks = TB / 1024;
   constexpr int kPer = kBlocks / 4;
   constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
   (void)nw;
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(ktile, TB), rv = tile_rsrc(vtile, TB);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int blk = w * kPer + i;  // rows blk*kRpb.. (K) / blk*8.. (V); the swizzle
                                    // phase depends on i only (w*kPer*kRpb % 16 == 0)
-    if (with_k) dma16(ktile + blk * 1024, k_lane_off<D>(i * kRpb, lane), buf + blk * 1024);
-    dma16(vtile + blk * 1024, v_lane_off(i * 8, lane), buf + Cfg<D>::kTileBytes + blk * 1024);
+    if (with_k) dma16b(rk, k_lane_off<D>(i * kRpb, lane), blk * 1024, buf + blk * 1024);
+    dma16b(rv, v_lane_off(i * 8, lane), blk * 1024, buf + TB + blk * 1024);
   }
 }
 
@@ -941,26 +956,28 @@ __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const 
 template <int D>
 __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const char* vtile, int kb,
                                          int wi, int nwv, int lane, bool with_k = true) {
+  constexpr int TB = Cfg<D>::kTileBytes;
   constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
   constexpr int KH = 32 * Cfg<D>::kRowBytes;   // bytes of a K half
   constexpr int kKBlocks = KH / 1024, kVBlocks = D * 64 / 1024;
   (void)nwv;
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(ktile, TB), rv = tile_rsrc(vtile, TB);
 #pragma unroll
   for (int i = 0; i < kKBlocks / 2; ++i) {
     const int blk = wi * (kKBlocks / 2) + i;   // swizzle phase depends on i only
     if (with_k)
-      dma16(ktile + (32 * kb) * Cfg<D>::kRowBytes + blk * 1024, k_lane_off<D>(i * kRpb, lane),
-            buf + blk * 1024);
+      dma16b(rk, k_lane_off<D>(i * kRpb, lane), (32 * kb) * Cfg<D>::kRowBytes + blk * 1024,
+             buf + blk * 1024);
   }
 #pragma unroll
   for (int i = 0; i < kVBlocks / 2; ++i) {
     const int blk = wi * (kVBlocks / 2) + i;
     // rows d = blk*16 + lane/4 (64-byte rows of 32 keys); chunk 4kb + c4 of the
-    // global 128-byte row
+    // global 128-byte row; the swizzle phase (d >> 2) & 3 = (lane >> 4) & 3
     const int d = blk * 16 + (lane >> 2);
     const int c4 = (lane & 3) ^ ((d >> 2) & 3);
     const uint32_t off = (uint32_t)((lane >> 2) * 128 + (c4 << 4));
-    dma16(vtile + blk * 16 * 128 + kb * 64, off, buf + KH + blk * 1024);
+    dma16b(rv, off, blk * 16 * 128 + kb * 64, buf + KH + blk * 1024);
   }
 }
 
