@@ -758,8 +758,9 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
 // 1 KB block of a tile, lane L writing LDS bytes [16L, 16L + 16) of the block,
 // so each lane fetches the global chunk that the swizzle places there.
 // Completion is tracked by vmcnt; LDS reads of other buffers need no wait.
-// Addresses are a wave-uniform base plus a 32-bit per-lane offset, so the
-// loads use the scalar-base form and the per-lane parts are a few registers.
+// This pointer form (the compiler forms 64-bit per-lane addresses) serves the
+// small MXFP4 copies of the skim tier; the bf16 K/V tiles use the buffer form
+// below.
 __device__ __forceinline__ void dma16(const char* gbase, uint32_t lane_off, char* lds_block) {
   __builtin_amdgcn_global_load_lds(gbase + lane_off, (VSA_LDS void*)lds_block, 16, 0, 0);
 }
