@@ -185,50 +185,114 @@ struct PlanArgs {
   Comb* comb;
 };
 
-// Exclusive scan of one int per thread over the 1024-thread block (wave scans
-// by lane shuffles, then a scan of the 16 wave sums); returns the thread's
-// prefix and the block total.  `ws` is 16 ints of LDS.
-__device__ int block_exclusive_scan(int v, int* ws, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Rows are taken in blocks of kPlanBlock = kPlanSeg * kPlanThreads.  Wave w
+// of the block holds its rows 512w + 64j + lane (j < kPlanSeg): consecutive
+// lanes read consecutive row_ptr entries and write consecutive unit records,
+// and row order is (wave, j, lane).  Row indices fit in 32 bits (rows * 64
+// tokens is checked against INT_MAX on the host), so all index arithmetic
+// here is 32-bit.
+constexpr int kPlanSeg = 8;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanBlock = kPlanSeg * kPlanThreads;
+
+__device__ __forceinline__ int plan_row(int c0, int j) {
+  return c0 + ((int)(threadIdx.x >> 6) << 9) + (j << 6) + (int)(threadIdx.x & 63);
+}
+
+// Lengths of this thread's rows of the block at c0 (-1 past the last row).
+__device__ __forceinline__ void load_lengths(const int* row_ptr, int rows, int c0,
+                                             int (&len)[kPlanSeg]) {
+  int a[kPlanSeg], b[kPlanSeg];
+#pragma unroll
+  for (int j = 0; j < kPlanSeg; ++j) {
+    const int r = min(plan_row(c0, j), rows);
+    a[j] = row_ptr[r];
+    b[j] = row_ptr[min(r + 1, rows)];
+  }
+#pragma unroll
+  for (int j = 0; j < kPlanSeg; ++j) len[j] = (plan_row(c0, j) < rows) ? b[j] - a[j] : -1;
+}
+
+// Exclusive prefix of a 0/1 count over the lanes of the wave, and the wave
+// total, by a ballot and bit counts.  Called by all 64 lanes.
+__device__ __forceinline__ int wave_prefix_flags(int v, int* total) {
+  const unsigned long long m = __ballot(v != 0);
+  *total = __popcll(m);
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The same for any count, by a shuffle scan.
+__device__ __forceinline__ int wave_prefix_scan(int v, int* total) {
+  const int lane = threadIdx.x & 63;
   int x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int y = __shfl_up(x, d);
     if (lane >= d) x += y;
   }
-  if (lane == 63) ws[w] = x;
-  __syncthreads();
-  if (w == 0) {
-    int s = (lane < kPlanThreads / 64) ? ws[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < kPlanThreads / 64; d <<= 1) {
-      const int y = __shfl_up(s, d);
-      if (lane >= d) s += y;
-    }
-    if (lane < kPlanThreads / 64) ws[lane] = s;
-  }
-  __syncthreads();
-  const int before = (w > 0) ? ws[w - 1] : 0;
-  *total = ws[kPlanThreads / 64 - 1];
-  __syncthreads();
-  return before + x - v;
+  *total = __shfl(x, 63);
+  return x - v;
 }
 
-// Rows are taken in blocks of kPlanSeg * kPlanThreads; thread t holds the
-// kPlanSeg consecutive rows starting at kPlanSeg * t of the block in registers.
-// Row indices fit in 32 bits (rows * 64 tokens is checked against INT_MAX on
-// the host), so all index arithmetic here is 32-bit, and the (batch, head) of
-// a row is tracked incrementally instead of divided out.
-constexpr int kPlanSeg = 8;
-constexpr int kPlanBlock = kPlanSeg * kPlanThreads;
+// Per-wave counts -> the sum over earlier waves (in place) and the block
+// totals.  `ws` holds NV * kPlanWaves ints of LDS.
+template <int NV>
+__device__ __forceinline__ void wave_offsets(int (&wt)[NV], int* ws, int (&total)[NV]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) ws[k * kPlanWaves + w] = wt[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanWaves; ++i) {
+      const int x = ws[k * kPlanWaves + i];
+      all += x;
+      before += (i < w) ? x : 0;
+    }
+    wt[k] = before;
+    total[k] = all;
+  }
+  __syncthreads();
+}
 
-__device__ __forceinline__ void load_lengths(const int* row_ptr, int rows, int r0,
-                                             int (&len)[kPlanSeg]) {
-  int ptr[kPlanSeg + 1];
+// Row-order exclusive prefix of NV per-row counts over the block (in place),
+// and the block totals; FLAGS: every count is 0 or 1.
+template <int NV, bool FLAGS>
+__device__ void block_prefix_rows(int (&v)[NV][kPlanSeg], int* ws, int (&total)[NV]) {
+  int wt[NV];
 #pragma unroll
-  for (int j = 0; j <= kPlanSeg; ++j) ptr[j] = row_ptr[min(rows, r0 + j)];
+  for (int k = 0; k < NV; ++k) {
+    int run = 0;
 #pragma unroll
-  for (int j = 0; j < kPlanSeg; ++j) len[j] = (r0 + j < rows) ? ptr[j + 1] - ptr[j] : -1;
+    for (int j = 0; j < kPlanSeg; ++j) {
+      int t;
+      const int pre = FLAGS ? wave_prefix_flags(v[k][j], &t) : wave_prefix_scan(v[k][j], &t);
+      v[k][j] = run + pre;
+      run += t;
+    }
+    wt[k] = run;
+  }
+  wave_offsets<NV>(wt, ws, total);
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int j = 0; j < kPlanSeg; ++j) v[k][j] += wt[k];
+}
+
+// Thread-order exclusive prefix of NV per-thread counts (in place), and totals.
+template <int NV>
+__device__ void block_prefix_threads(int (&v)[NV], int* ws, int (&total)[NV]) {
+  int wt[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = wave_prefix_scan(v[k], &wt[k]);
+  wave_offsets<NV>(wt, ws, total);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] += wt[k];
 }
 
 // Work plan of one call: G units (pairs of complete rows of one (batch, head),
@@ -237,14 +301,16 @@ __device__ __forceinline__ void load_lengths(const int* row_ptr, int rows, int r
 // combine entries.  Pass 1 scans the complete rows (their count before each
 // (batch, head)) and totals the S units of the other rows; the per-(batch,
 // head) scan then fixes the pairing, the G chunking and every total; pass 2
-// places each row.
+// places each row.  CHUNKED: S rows are cut into kv_chunk keys (a row may
+// then give several units); otherwise each S row is one unit.
+template <bool CHUNKED>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
-  __shared__ int ws[kPlanThreads / 64];
+  __shared__ int ws[5 * kPlanWaves];
   __shared__ int s_chunk_g, s_sg, s_front;
   const int nT = p.nT;  // >= 1
   const int t = threadIdx.x;
   const int rows = p.bh * nT;
-  const bool chunked = p.kv_chunk > 0;
+  constexpr bool chunked = CHUNKED;
   const int chunk_s = p.kv_chunk;
   // S chunks of a row of `len` keys, and the key count of chunk c
   auto n_chunks = [&](int len) { return (!chunked || len <= 0) ? 1 : (len + chunk_s - 1) / chunk_s; };
@@ -265,41 +331,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   if (t == 0) s_front = 0;
 
   // pass 1: cbase[b] = complete rows before (b, h) (a scan of the complete-row
-  // flags in row order), and the S totals of the incomplete rows
+  // flags in row order), and the S totals of the incomplete rows.  With a
+  // single block the lengths stay in registers for pass 2.
+  const bool one_block = rows <= kPlanBlock;
+  int len[kPlanSeg];
   int a_units = 0, a_front = 0, a_slots = 0, a_comb = 0;
   int carry_c = 0;
   for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
-    const int r0 = c0 + kPlanSeg * t;
-    int len[kPlanSeg];
-    load_lengths(p.row_ptr, rows, r0, len);
-    int n_c = 0;
+    load_lengths(p.row_ptr, rows, c0, len);
+    int before[1][kPlanSeg];
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) n_c += (len[j] == nT);
-    int blk_c;
-    int e = carry_c + block_exclusive_scan(n_c, ws, &blk_c);
-    int b = min(r0, rows) / nT, pos = min(r0, rows) - b * nT;  // (b, h) of row r0 + j, offset in it
+    for (int j = 0; j < kPlanSeg; ++j) before[0][j] = (len[j] == nT);
+    int blk[1];
+    block_prefix_rows<1, true>(before, ws, blk);
 #pragma unroll
     for (int j = 0; j < kPlanSeg; ++j) {
-      if (len[j] >= 0) {
-        if (pos == 0) p.cbase[b] = e;
-        if (len[j] == nT) {
-          ++e;
-        } else {
-          const int n = n_chunks(len[j]);
-          a_units += n;
-          a_front += n_front_of(len[j], n);
-          if (n > 1) {
-            a_slots += n;
-            a_comb += 1;
-          }
+      if (len[j] < 0) continue;
+      const int r = plan_row(c0, j);
+      const int b = r / nT;
+      if (r == b * nT) p.cbase[b] = carry_c + before[0][j];
+      if (len[j] != nT) {
+        const int n = n_chunks(len[j]);
+        a_units += n;
+        a_front += n_front_of(len[j], n);
+        if (n > 1) {
+          a_slots += n;
+          a_comb += 1;
         }
       }
-      if (++pos == nT) {
-        pos = 0;
-        ++b;
-      }
     }
-    carry_c += blk_c;
+    carry_c += blk[0];
   }
   if (t == 0) p.cbase[p.bh] = carry_c;
   __syncthreads();
@@ -323,17 +384,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       }
     }
   }
-  int NG;
-  int gb = block_exclusive_scan(g_sum, ws, &NG);
+  int tv[5] = {g_sum, a_units, a_front, a_slots, a_comb};
+  int tot[5];
+  block_prefix_threads<5>(tv, ws, tot);
+  const int NG = tot[0], nSU = tot[1], nFront = tot[2], nSP = tot[3], nSC = tot[4];
+  int gb = tv[0];
   for (int b = b0; b < b1; ++b) {
     p.gbase[b] = gb;
     gb += count_of(b) / 2;
   }
-  int nSU, nFront, nSP, nSC;
-  (void)block_exclusive_scan(a_units, ws, &nSU);
-  (void)block_exclusive_scan(a_front, ws, &nFront);
-  (void)block_exclusive_scan(a_slots, ws, &nSP);
-  (void)block_exclusive_scan(a_comb, ws, &nSC);
   if (t == 0) {
     int chunk;
     if (chunked) {
@@ -381,88 +440,85 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   int carry_rest = 0, carry_slot = 0, carry_comb = 0;
   carry_c = 0;
   for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
-    const int r0 = c0 + kPlanSeg * t;
-    int len[kPlanSeg];
-    load_lengths(p.row_ptr, rows, r0, len);
-    int n_c = 0;
+    if (!one_block) load_lengths(p.row_ptr, rows, c0, len);
+    int before[1][kPlanSeg];
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) n_c += (len[j] == nT);
-    int blk_c;
-    int e = carry_c + block_exclusive_scan(n_c, ws, &blk_c);
-    // pairing data of the segment's first (b, h), which every row shares but
-    // those past a (b, h) boundary
-    const int bf = min(r0, rows - 1) / nT;
-    const int cb_f = p.cbase[bf], cnt_f = p.cbase[bf + 1] - cb_f, gb_f = p.gbase[bf];
-    int b = bf, pos = min(r0, rows - 1) - bf * nT;
-    int nS[kPlanSeg];  // S chunks of the row, 0 for G members and padding
-    int v_rest = 0, v_slot = 0, v_comb = 0;
+    for (int j = 0; j < kPlanSeg; ++j) before[0][j] = (len[j] == nT);
+    int blk_c[1];
+    block_prefix_rows<1, true>(before, ws, blk_c);
+    // per row: rest-region units, then (CHUNKED) partial slots and combine entries
+    constexpr int NC = CHUNKED ? 3 : 1;
+    int nS[kPlanSeg];            // S chunks of the row, 0 for G members and padding
+    int cnt[NC][kPlanSeg];
 #pragma unroll
     for (int j = 0; j < kPlanSeg; ++j) {
       nS[j] = 0;
-      if (len[j] >= 0) {
-        bool g_member = false;
-        if (len[j] == nT) {
-          const int cb_r = (b == bf) ? cb_f : p.cbase[b];
-          const int cnt_r = (b == bf) ? cnt_f : p.cbase[b + 1] - cb_r;
-          const int gb_r = (b == bf) ? gb_f : p.gbase[b];
-          const int jj = e - cb_r;  // index among the complete rows of (b, h)
-          ++e;
-          if (jj < (cnt_r / 2) * 2) {
-            p.grows[(gb_r + jj / 2) * 2 + (jj & 1)] = r0 + j;
-            g_member = true;
-          }
-        }
-        if (!g_member) {
-          const int n = n_chunks(len[j]);
-          nS[j] = n;
-          v_rest += n - n_front_of(len[j], n);
-          if (n > 1) {
-            v_slot += n;
-            v_comb += 1;
-          }
+#pragma unroll
+      for (int k = 0; k < NC; ++k) cnt[k][j] = 0;
+      const int r = plan_row(c0, j);
+      const int b = min(r, rows - 1) / nT;
+      const int cb_r = p.cbase[b], cnt_r = p.cbase[b + 1] - cb_r, gb_r = p.gbase[b];
+      if (len[j] < 0) continue;
+      bool g_member = false;
+      if (len[j] == nT) {
+        const int jj = carry_c + before[0][j] - cb_r;  // index among the complete rows of (b, h)
+        if ((unsigned)jj < (unsigned)((cnt_r / 2) * 2)) {
+          p.grows[(gb_r + jj / 2) * 2 + (jj & 1)] = r;
+          g_member = true;
         }
       }
-      if (++pos == nT) {
-        pos = 0;
-        ++b;
+      if (!g_member) {
+        const int n = n_chunks(len[j]);
+        nS[j] = n;
+        cnt[0][j] = n - n_front_of(len[j], n);
+        if constexpr (CHUNKED) {
+          if (n > 1) {
+            cnt[1][j] = n;
+            cnt[2][j] = 1;
+          }
+        }
       }
     }
-    int blk_rest, blk_slot, blk_comb;
-    int pos_rest = carry_rest + block_exclusive_scan(v_rest, ws, &blk_rest);
-    int pos_slot = carry_slot + block_exclusive_scan(v_slot, ws, &blk_slot);
-    int pos_comb = carry_comb + block_exclusive_scan(v_comb, ws, &blk_comb);
+    int blk[NC];
+    block_prefix_rows<NC, !CHUNKED>(cnt, ws, blk);
 #pragma unroll
     for (int j = 0; j < kPlanSeg; ++j) {
       const int n = nS[j];
       if (n == 0) continue;
-      const int r = r0 + j;
+      const int r = plan_row(c0, j);
+      int pos_rest = carry_rest + cnt[0][j];
+      int slot0 = -1;
+      if constexpr (CHUNKED) slot0 = gsl + carry_slot + cnt[1][j];
       for (int c = 0; c < n; ++c) {
         Unit u;
         u.row[0] = r;
         u.row[1] = -1;
         u.kb = (n > 1) ? c * chunk_s : 0;
         u.ke = u.kb + chunk_len(len[j], n, c);
-        u.slot = (n > 1) ? gsl + pos_slot + c : -1;
+        u.slot = (n > 1) ? slot0 + c : -1;
         u.mode = 1;
         u.pad[0] = u.pad[1] = 0;
         const int at = is_front(u.ke - u.kb) ? atomicAdd(&s_front, 1) : rest_base + pos_rest++;
-        p.units[at] = u;
+        if ((unsigned)at < (unsigned)n_units) p.units[at] = u;
       }
-      if (n > 1) {
-        Comb cb2;
-        cb2.row = r;
-        cb2.slot0 = gsl + pos_slot;
-        cb2.stride = 1;
-        cb2.n = n;
-        p.comb[comb_base + pos_comb] = cb2;
-        pos_slot += n;
-        ++pos_comb;
+      if constexpr (CHUNKED) {
+        if (n > 1) {
+          Comb cb2;
+          cb2.row = r;
+          cb2.slot0 = slot0;
+          cb2.stride = 1;
+          cb2.n = n;
+          const int ci = comb_base + carry_comb + cnt[2][j];
+          if ((unsigned)ci < (unsigned)n_comb) p.comb[ci] = cb2;
+        }
       }
     }
-    carry_c += blk_c;
-    carry_rest += blk_rest;
-    carry_slot += blk_slot;
-    carry_comb += blk_comb;
+    carry_c += blk_c[0];
+    carry_rest += blk[0];
+    if constexpr (CHUNKED) {
+      carry_slot += blk[1];
+      carry_comb += blk[2];
+    }
   }
   __syncthreads();
 
@@ -1285,7 +1341,10 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   pa.W = s.W;
   pa.units = reinterpret_cast<Unit*>(w + L.off_units);
   pa.comb = reinterpret_cast<Comb*>(w + L.off_comb);
-  plan_kernel<<<1, kPlanThreads, 0, stream>>>(pa);
+  if (kv_chunk > 0)
+    plan_kernel<true><<<1, kPlanThreads, 0, stream>>>(pa);
+  else
+    plan_kernel<false><<<1, kPlanThreads, 0, stream>>>(pa);
 
   AttnArgs aa;
   aa.q = static_cast<const uint16_t*>(q);

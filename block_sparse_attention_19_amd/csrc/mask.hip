@@ -13,7 +13,8 @@
 //                 The row length in closed form (nT if routed, else the
 //                 clipped window count) goes to row_ptr[row + 1].
 //   2. scan    -- in-place exclusive scan of the lengths -> row_ptr.  One
-//                 workgroup, a shuffle block scan per chunk of rows.
+//                 workgroup, a shuffle block scan per chunk of rows staged
+//                 through LDS (coalesced global reads and writes).
 //   3. fill    -- one wave per row writes the ascending key-tile list: 0..nT-1
 //                 for a routed row, else the window enumerated as runs of
 //                 consecutive tw for each (dt, dh), which is ascending tile order.
@@ -110,25 +111,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
 
 // In-place scan of the row lengths in row_ptr[1..rows] (row_ptr[0] = 0), so
 // that row_ptr becomes their exclusive scan.  Rows are taken in chunks of
-// kScanRowsPerThread * kScanThreads, each thread holding kScanRowsPerThread
-// consecutive lengths in registers; a block scan of the per-thread sums plus
-// the running total of earlier chunks gives each thread its offset.
+// kScanRowsPerThread * kScanThreads: the chunk is staged in LDS by coalesced
+// loads, each thread scans kScanRowsPerThread consecutive lengths in
+// registers, a block scan of the per-thread sums plus the running total of
+// earlier chunks gives each thread its offset, and the results leave through
+// LDS by coalesced stores.
 __global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(int64_t rows,
                                                                     int* __restrict__ row_ptr) {
   constexpr int kChunk = kScanRowsPerThread * kScanThreads;
   __shared__ int sums[kScanThreads / 64];
+  __shared__ int stage[kChunk];
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
   int* len_p = row_ptr + 1;
   int carry = 0;
   for (int64_t c0 = 0; c0 < rows; c0 += kChunk) {
     const int n = (int)min<int64_t>(kChunk, rows - c0);
+#pragma unroll
+    for (int j = 0; j < kScanRowsPerThread; ++j) {
+      const int i = t + j * kScanThreads;
+      stage[i] = (i < n) ? len_p[c0 + i] : 0;
+    }
+    __syncthreads();
     int len[kScanRowsPerThread];
     int local = 0;
 #pragma unroll
     for (int j = 0; j < kScanRowsPerThread; ++j) {
-      const int i = kScanRowsPerThread * t + j;
-      len[j] = (i < n) ? len_p[c0 + i] : 0;
+      len[j] = stage[kScanRowsPerThread * t + j];
       local += len[j];
     }
     // lane shuffles within each wave, then a scan of the wave totals by the
@@ -154,11 +163,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_lengths_kernel(int64_t rows
     int run = carry + ((wv > 0) ? sums[wv - 1] : 0) + x - local;
 #pragma unroll
     for (int j = 0; j < kScanRowsPerThread; ++j) {
-      const int i = kScanRowsPerThread * t + j;
       run += len[j];
-      if (i < n) len_p[c0 + i] = run;
+      stage[kScanRowsPerThread * t + j] = run;
     }
     carry += sums[kScanThreads / 64 - 1];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kScanRowsPerThread; ++j) {
+      const int i = t + j * kScanThreads;
+      if (i < n) len_p[c0 + i] = stage[i];
+    }
     __syncthreads();
   }
 }
