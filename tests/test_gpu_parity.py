@@ -226,6 +226,24 @@ def test_attention_large_sampled(cid, ki):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("heads,kv_chunk", [(32, 0), (33, 0), (33, 64)])
+def test_attention_plan_block_boundary(heads, kv_chunk):
+    """The work plan takes rows in blocks of 8192: exactly one full block
+    (32 heads x 256 tiles), and one row of tiles past it (33 heads), with
+    every row cut into key chunks in the last case.  51 routed tiles per head
+    (an odd count: one complete row is left over from the pairing)."""
+    T, H, W, D = 32, 32, 16, 64
+    w = wl.custom(T, H, W, heads, D, radius_set=(1, 2, 3), cid=413)
+    kcount = 51
+    say(f"attention plan blocks T={T} H={H} W={W} heads={heads} k={kcount} kv_chunk={kv_chunk}")
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    out = _run_all(w, q, k, v, r, s, kcount, kv_chunk=kv_chunk)
+    _check_sampled(w, q, k, v, r, s, kcount, out, heads=sorted({0, 31, heads - 1}), seed=heads)
+    del out
+    torch.cuda.empty_cache()
+
+
 def test_attention_batch2_full():
     """Two batch entries with different inputs, radii and scores (the
     workloads draw B = 1; the batch axis stacks two draws)."""
