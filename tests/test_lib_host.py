@@ -81,6 +81,14 @@ def test_validation_rejects_before_launch():
     s96 = vsa.shape(1, 2, 96, 8, 16, 16)
     assert L.vsa_tile_permute(ctypes.byref(s96), good, good, 0, None) == UNSUPPORTED
     assert L.vsa_tile_permute(None, good, good, 0, None) == INVALID
+    # empty grids and zero batch / heads are rejected, not launched
+    for dims in ((1, 2, 64, 0, 16, 16), (1, 2, 64, 8, 0, 16), (1, 2, 64, 8, 16, 0),
+                 (0, 2, 64, 8, 16, 16), (1, 0, 64, 8, 16, 16)):
+        se = ctypes.byref(vsa.shape(*dims))
+        assert L.vsa_tile_permute(se, good, good, 0, None) == INVALID
+        assert L.vsa_num_tiles(se) == -1
+        assert L.vsa_attn_fwd(se, good, good, good, good, good, 0.125, good, None, 0, good,
+                              1 << 20, None) == INVALID
     # mask: dense_count, r_max, capacity
     nT = 32
     cap = vsa.mask_nnz_bound(s, 3, 6)
