@@ -24,6 +24,12 @@ What is computed, and where it comes from:
   block-sparse execution of TRA step 3 and of the other pages skips masked
   tiles and must reach this same result.
 
+* Exact per-token windows -- TRA, pipeline steps 2 and 3: radii are
+  assigned per query token and translated into block masks.  The block mask
+  uses each tile's largest token radius; the exact variant lets every query
+  token attend only the key tiles of its own radius's window (routed tiles
+  still attend every key tile).
+
 * Low-precision tier -- "Triage: Skip, Skim, or Refine Attention Tiles in
   Video Diffusion Transformers": each kept tile pair is either computed in a
   quick 4-bit version (skim) or fully (refine).  Reading adopted here: an
@@ -418,3 +424,52 @@ def tile_score_from_tokens(token_score: np.ndarray, T: int, H: int, W: int) -> n
     # back from the key to the float's bits (total_order_key inverted)
     bits = np.where(best >= 2 ** 31, best - 2 ** 31, (~best) & 0xFFFFFFFF).astype(np.uint32)
     return bits.view(np.float32)
+
+
+# ----------------------------------------------------- exact per-token windows
+#
+# TRA, pipeline step 3, turns the token-level radii into block masks; the
+# block mask of a tile uses the largest radius among its tokens, so it holds
+# every token's window.  Reading adopted for the exact variant: query token i
+# attends the real key tokens of the key tiles inside the window of its own
+# radius r_i (clamped to r_max like the tile radii) around its tile -- the
+# tile_keep rule with r_i -- or of every key tile if its tile is routed.
+
+def token_window_keep(token_radius: np.ndarray, routed: np.ndarray, r_max: int,
+                      T: int, H: int, W: int) -> np.ndarray:
+    """Bool [N, nT]: does query token i attend to key tile b."""
+    tt = token_tile(T, H, W)
+    n = num_tiles(T, H, W)
+    r = np.minimum(np.asarray(token_radius, dtype=np.int64), r_max)
+    out = np.zeros((len(tt), n), dtype=bool)
+    for rv in np.unique(r):
+        sel = r == rv
+        out[sel] = tile_keep(np.full(n, rv), routed, T, H, W)[tt[sel]]
+    return out
+
+
+def token_window_attention_rows(q, k, v, keep_tok: np.ndarray, tok_tile: np.ndarray,
+                                rows: np.ndarray, scale: float):
+    """Rows ``rows`` of one head under per-token windows keep_tok [N, nT]."""
+    return masked_attention_rows(q[rows], k, v, keep_tok[rows][:, tok_tile], scale)
+
+
+def token_window_attention(q_bits, k_bits, v_bits, token_radius, scores, k: int, r_max: int,
+                           T: int, H: int, W: int, scale: float):
+    """Every valid query of every (b, h) under per-token windows.  token_radius:
+    uint8 [B, Hh, N] (raster order); scores: float32 [B, Hh, nT] tile routing
+    scores.  Returns O float64 [B, N, Hh, D] and LSE [B, Hh, N]."""
+    B, N, Hh, _ = q_bits.shape
+    tt = token_tile(T, H, W)
+    O = np.zeros((B, N, Hh, v_bits.shape[-1]))
+    L = np.zeros((B, Hh, N))
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(Hh):
+            keep_tok = token_window_keep(token_radius[b, h], routed_tiles(scores[b, h], k),
+                                         r_max, T, H, W)
+            q = bf16_to_f64(q_bits[b, :, h])
+            kk = bf16_to_f64(k_bits[b, :, h])
+            vv = bf16_to_f64(v_bits[b, :, h])
+            O[b, :, h], L[b, h] = token_window_attention_rows(q, kk, vv, keep_tok, tt, rows, scale)
+    return O, L
