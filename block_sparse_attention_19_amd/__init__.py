@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "vsa_quantize_mxfp4": (ctypes.c_int, [SP, P, P, P, P]),
         "vsa_attn_fwd_tiered": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, I32, P, SZ, P]),
+        "vsa_attn_fwd_token_window": (ctypes.c_int, [SP, P, P, P, P, P, P, P, I32, ctypes.c_float,
+                                                     P, P, I32, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -340,6 +342,54 @@ def attn_fwd_tiered(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
                                      _ptr(col_idx), _ptr(tier), scale, _ptr(out), _ptr(lse),
                                      kv_chunk, _ptr(workspace), workspace.numel(), _stream(dev)),
            "vsa_attn_fwd_tiered")
+    return out, lse
+
+
+def attn_fwd_token_window(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
+                          row_ptr: torch.Tensor, col_idx: torch.Tensor, routed: torch.Tensor,
+                          token_radius: torch.Tensor, s: Shape, r_max: int,
+                          scale: Optional[float] = None, kv_chunk: int = 0,
+                          with_lse: bool = True, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """attn_fwd with exact per-token windows: each query token attends only the
+    kept key tiles inside the window of its own radius min(token_radius, r_max)
+    (routed query tiles attend every kept key tile).  routed uint8 [B, heads,
+    nT] and the CSR come from build_mask on tile radii that cover the token
+    radii (tile_radius_from_tokens) with the same r_max; token_radius uint8
+    [B, heads, T*H*W] in raster order."""
+    q_t = _require(q_t, torch.bfloat16, "q_t")
+    k_t = _require(k_t, torch.bfloat16, "k_t")
+    v_t = _require(v_t, torch.bfloat16, "v_t")
+    row_ptr = _require(row_ptr, torch.int32, "row_ptr")
+    col_idx = _require(col_idx, torch.int32, "col_idx")
+    routed = _require(routed, torch.uint8, "routed")
+    nT = num_tiles(s)
+    D = s.head_dim
+    tok = (s.batch, s.heads, nT * 64, D)
+    if q_t.shape != tok or k_t.shape != tok or v_t.shape != (s.batch, s.heads, nT, D, 64):
+        raise ValueError("q_t / k_t / v_t shapes do not match the shape")
+    if row_ptr.numel() != s.batch * s.heads * nT + 1:
+        raise ValueError("row_ptr must have B*heads*nT + 1 entries")
+    if routed.numel() != s.batch * s.heads * nT:
+        raise ValueError("routed must be [B, heads, nT]")
+    token_radius = _token_array(token_radius, s, torch.uint8, "token_radius")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q_t.device
+    if out is None:
+        out = torch.empty(tok, dtype=torch.bfloat16, device=dev)
+    lse = lse_out
+    if lse is None and with_lse:
+        lse = torch.empty(tok[:3], dtype=torch.float32, device=dev)
+    ws_bytes = attn_workspace_bytes(s, kv_chunk)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(lib().vsa_attn_fwd_token_window(ctypes.byref(s), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+                                           _ptr(row_ptr), _ptr(col_idx), _ptr(routed),
+                                           _ptr(token_radius), int(r_max), scale, _ptr(out),
+                                           _ptr(lse), kv_chunk, _ptr(workspace),
+                                           workspace.numel(), _stream(dev)),
+           "vsa_attn_fwd_token_window")
     return out, lse
 
 

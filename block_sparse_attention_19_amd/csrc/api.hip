@@ -341,4 +341,51 @@ vsa_status vsa_attn_fwd_tiered(const vsa_shape* s, const void* q_t, const void* 
                     "attention launch");
 }
 
+vsa_status vsa_attn_fwd_token_window(const vsa_shape* s, const void* q_t, const void* k_t,
+                                     const void* v_t, const int32_t* row_ptr,
+                                     const int32_t* col_idx, const uint8_t* routed,
+                                     const uint8_t* token_radius, int32_t r_max, float scale,
+                                     void* o_t, float* lse_t, int32_t kv_chunk, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  VSA_TRY(check_shape(s));
+  VSA_TRY(check_ptr(q_t, 16, "q_t"));
+  VSA_TRY(check_ptr(k_t, 16, "k_t"));
+  VSA_TRY(check_ptr(v_t, 16, "v_t"));
+  VSA_TRY(check_ptr(row_ptr, 4, "row_ptr"));
+  VSA_TRY(check_ptr(col_idx, 4, "col_idx"));
+  VSA_TRY(check_ptr(routed, 1, "routed"));
+  VSA_TRY(check_ptr(token_radius, 1, "token_radius"));
+  VSA_TRY(check_ptr(o_t, 16, "o_t"));
+  if (lse_t) VSA_TRY(check_ptr(lse_t, 4, "lse_t"));
+  VSA_TRY(check_ptr(ws, 256, "ws"));
+  if (!(scale > 0.f) || scale > 3.0e38f) {
+    set_error("scale must be finite and > 0");
+    return VSA_ERR_INVALID_ARG;
+  }
+  if (kv_chunk < 0) {
+    set_error("kv_chunk must be >= 0");
+    return VSA_ERR_INVALID_ARG;
+  }
+  if (r_max < 0 || r_max > 255) {
+    set_error("r_max %d outside [0, 255]", r_max);
+    return VSA_ERR_INVALID_ARG;
+  }
+  const Grid g = make_grid(*s);
+  if (g.nt >= 1024 || g.nh >= 1024 || g.nw >= 1024) {
+    set_error("token windows take grids below 1024 tiles along each axis");
+    return VSA_ERR_UNSUPPORTED;
+  }
+  const size_t need = attn_layout(*s, kv_chunk).total;
+  if (ws_bytes < need) {
+    set_error("attention workspace %zu < %zu bytes", ws_bytes, need);
+    return VSA_ERR_CAPACITY;
+  }
+  int cus = 0;
+  VSA_TRY(device_cus(&cus));
+  const TokenWindows tw = {token_radius, routed, r_max};
+  return hip_status(launch_attn(*s, q_t, k_t, v_t, row_ptr, col_idx, scale, o_t, lse_t, kv_chunk,
+                                ws, cus, static_cast<hipStream_t>(stream), nullptr, &tw),
+                    "attention launch");
+}
+
 }  // extern "C"

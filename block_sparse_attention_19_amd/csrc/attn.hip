@@ -137,6 +137,23 @@ __device__ __forceinline__ TileExtent tile_extent(int tau, int nh, int nw, int T
 
 }  // namespace
 
+// Packed tile coordinates tt | th << 10 | tw << 20 (each below 1024; the entry
+// point taking token windows checks the grid).
+__device__ __forceinline__ int pack_coord(int tau, int nh, int nw) {
+  const int tw = tau % nw, th = (tau / nw) % nh, tt = tau / (nw * nh);
+  return tt | (th << 10) | (tw << 20);
+}
+
+// Window distance of key tile c from query tile qc (packed coordinates): key
+// tile c lies in the window of radius r around qc iff r >= this value (the
+// rule |dt| <= r, max(|dh|, |dw|) <= r - |dt| rearranged).
+__device__ __forceinline__ int window_dist(int c, int qc) {
+  const int dt = abs((c & 1023) - (qc & 1023));
+  const int dh = abs(((c >> 10) & 1023) - ((qc >> 10) & 1023));
+  const int dw = abs(((c >> 20) & 1023) - ((qc >> 20) & 1023));
+  return dt + max(dh, dw);
+}
+
 // ------------------------------------------------------------ workspace
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -166,6 +183,7 @@ AttnLayout attn_layout(const vsa_shape& s, int kv_chunk) {
   L.off_po = take((size_t)L.max_slots * kTileTokens * s.head_dim * 4);
   L.off_pml = take((size_t)L.max_slots * kTileTokens * 2 * 4);
   L.off_ext = take(4 * (size_t)g.nT);
+  L.off_coord = take(4 * (size_t)g.nT);
   L.total = o;
   return L;
 }
@@ -180,7 +198,7 @@ struct PlanArgs {
   int nh, nw, T, H, W;
   int64_t max_units, max_slots;
   Header* hdr;
-  int *cbase, *gbase, *grows, *ext;
+  int *cbase, *gbase, *grows, *ext, *coord;
   Unit* units;
   Comb* comb;
 };
@@ -327,7 +345,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     return f;
   };
 
-  for (int tau = t; tau < nT; tau += kPlanThreads) p.ext[tau] = pack_extent(tau, p.nh, p.nw, p.T, p.H, p.W);
+  for (int tau = t; tau < nT; tau += kPlanThreads) {
+    p.ext[tau] = pack_extent(tau, p.nh, p.nw, p.T, p.H, p.W);
+    p.coord[tau] = pack_coord(tau, p.nh, p.nw);
+  }
   if (t == 0) s_front = 0;
 
   // pass 1: cbase[b] = complete rows before (b, h) (a scan of the complete-row
@@ -580,6 +601,11 @@ struct AttnArgs {
   const uint8_t* k4;
   const uint8_t* k4s;
   const uint8_t* tier; // [nnz], 1 = skim
+  // exact per-token windows (token-window instance only)
+  const int* coord;     // packed coordinates per key tile
+  const uint8_t* tok_r; // token radii [BH][T*H*W], raster order
+  const uint8_t* routed;// routed flag per CSR row
+  int r_max;
   int nT, nh, nw, T, H, W;
   float c2;            // scale * log2(e)
 };
@@ -655,6 +681,7 @@ struct WaveState {
   float l;  // this lane's partial sum of P
   i32x4 q4[D / 64];  // skim tier: MXFP4 Q fragments (B operands)
   int q4s;           // their scales, shifted so that byte 2m is fragment m's
+  int rl;            // token-window instance: this lane's query radius (255: no limit)
 };
 
 // This wave's Q fragments (B operands of S^T = K Q^T): row q of its 32 query
@@ -749,10 +776,10 @@ __device__ __forceinline__ float sum_halves(float x) {
 // i.e. lt = 2kb + r/8, lh = 2h + (r/4)%2, lw = r%4.
 // HALF_V: `vbuf` holds only the 32 keys of this half ([D][32], vh_off);
 // otherwise the whole tile ([D][64], v_off).
-template <int D, bool HALF_V>
+template <int D, bool HALF_V, bool TOKR = false>
 __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, const char* vbuf,
                                                 int kb, int lane, const TileExtent& ext,
-                                                float c2) {
+                                                float c2, int dist = 0) {
   const int q = lane & 31, h = lane >> 5;
   if (ext.edge) {
     const bool h_ok0 = 2 * h < ext.vh, h_ok1 = 2 * h + 1 < ext.vh;
@@ -761,6 +788,15 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
       const bool tw_ok = ((2 * kb + (r >> 3)) < ext.vt) && ((r & 3) < ext.vw);
       const bool ok = tw_ok && ((r & 4) ? h_ok1 : h_ok0);
       s[r] = ok ? s[r] : -INFINITY;
+    }
+  }
+  if constexpr (TOKR) {
+    // exact per-token windows: this lane's query attends the key tile only if
+    // the tile lies inside the window of the query's own radius
+    if (!__all(st.rl >= dist)) {
+      const bool in = st.rl >= dist;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = in ? s[r] : -INFINITY;
     }
   }
   // This lane's 16 scores decide whether the running max must move: the
@@ -782,8 +818,10 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
       for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     st.m = mn;
   }
-  // every tile holds at least one valid key, so the running max is finite here
-  const float mneg = -st.m;
+  // every tile holds at least one valid key, so the running max is finite here;
+  // with per-token windows a lane may not have met an attended tile yet (all
+  // its scores so far -inf): its probabilities are then exp2(-inf) = 0
+  const float mneg = (TOKR && st.m == -INFINITY) ? 0.f : -st.m;
   bf16x8 pb[2];
   float pf[16];
 #pragma unroll
@@ -921,11 +959,11 @@ __device__ __forceinline__ int tier2(const SkimRef& sk, int i) {
 // MXFP4 K (into the buffers past the bf16 ones) only if a row skims it.  V is
 // always bf16.  Each query tile's waves take the products of their own row's
 // tier.
-template <int D, int CUR, bool TIER>
+template <int D, int CUR, bool TIER, bool TOKR>
 __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int code, int tc,
                                        int tn, const char* kbase, const char* vbase,
                                        const SkimRef& sk, const AttnArgs& a, int wave, int lane,
-                                       int grp) {
+                                       int grp, int dist) {
   constexpr int TB = Cfg<D>::kTileBytes;
   const char* kbuf = smem + CUR * Cfg<D>::kSplitBytes;
   const char* vbuf = kbuf + TB;
@@ -950,8 +988,8 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int
     s0 = qk32<D>(kbuf, st, lane);
     s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
   }
-  softmax_pv_half<D, false>(st, s0, vbuf, 0, lane, ext, a.c2);
-  softmax_pv_half<D, false>(st, s1, vbuf, 1, lane, ext, a.c2);
+  softmax_pv_half<D, false, TOKR>(st, s0, vbuf, 0, lane, ext, a.c2, dist);
+  softmax_pv_half<D, false, TOKR>(st, s1, vbuf, 1, lane, ext, a.c2, dist);
   wait_dma();
   lds_barrier();
 }
@@ -961,15 +999,16 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int
 // streams into the other (a whole step to arrive, one barrier per step).
 // Column indices are read two tiles ahead and the next tile's extent one
 // tile ahead, so neither load is waited on.
-template <int D, bool TIER>
+template <int D, bool TIER, bool TOKR>
 __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const int* cols,
                                             int nkeys, const char* kbase, const char* vbase,
                                             const SkimRef& sk, const AttnArgs& a, int wave,
-                                            int lane, const uint16_t* qp, int grp) {
+                                            int lane, const uint16_t* qp, int grp, int qc) {
   constexpr int TB = Cfg<D>::kTileBytes;
   const int j0 = uni(cols[0]);
   int jn = (1 < nkeys) ? uni(cols[1]) : -1;
   int code = uni(a.ext[j0]);
+  int cc = TOKR ? uni(a.coord[j0]) : 0;  // coordinates of the current key tile
   int tc = 0, tn = 0;  // tier bits of the current and the next tile (tiered instance)
   if constexpr (TIER) {
     tc = uni(tier2(sk, 0));
@@ -988,19 +1027,25 @@ __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const 
   for (int step = 0; step < nkeys; step += 2) {
     int jnn_v = (step + 2 < nkeys) ? cols[step + 2] : -1;
     int cn_v = (jn >= 0) ? a.ext[jn] : 0;
+    int ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
     int tnn_v = 0;
     if constexpr (TIER) tnn_v = (step + 2 < nkeys) ? tier2(sk, step + 2) : 0;
-    g_step<D, 0, TIER>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp);
+    g_step<D, 0, TIER, TOKR>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp,
+                             TOKR ? window_dist(cc, qc) : 0);
     code = uni(cn_v);
+    cc = uni(ccn_v);
     jn = uni(jnn_v);
     tc = tn;
     tn = uni(tnn_v);
     if (step + 1 >= nkeys) break;
     jnn_v = (step + 3 < nkeys) ? cols[step + 3] : -1;
     cn_v = (jn >= 0) ? a.ext[jn] : 0;
+    ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
     if constexpr (TIER) tnn_v = (step + 3 < nkeys) ? tier2(sk, step + 3) : 0;
-    g_step<D, 1, TIER>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp);
+    g_step<D, 1, TIER, TOKR>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp,
+                             TOKR ? window_dist(cc, qc) : 0);
     code = uni(cn_v);
+    cc = uni(ccn_v);
     jn = uni(jnn_v);
     tc = tn;
     tn = uni(tnn_v);
@@ -1044,11 +1089,11 @@ __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const cha
 // so the two tiles a step needs fit beside their prefetches.  Tiered
 // instance: a skim tile brings its MXFP4 K half instead of the bf16 one, into
 // the split's half buffers past the bf16 region.
-template <int D, bool TIER>
+template <int D, bool TIER, bool TOKR>
 __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const int* cols,
                                             int nkeys, const char* kbase, const char* vbase,
                                             const SkimRef& sk, const AttnArgs& a, int wave,
-                                            int lane, int grp, const uint16_t* qp) {
+                                            int lane, int grp, const uint16_t* qp, int qc) {
   constexpr int TB = Cfg<D>::kTileBytes;
   constexpr int KH = 32 * Cfg<D>::kRowBytes;
   constexpr int BUF = KH + D * 64;                       // one half-tile buffer
@@ -1062,6 +1107,7 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
   int j = (grp < nkeys) ? uni(cols[grp]) : -1;
   int jn = (2 + grp < nkeys) ? uni(cols[2 + grp]) : -1;
   int code = (j >= 0) ? uni(a.ext[j]) : 0;
+  int cc = (TOKR && j >= 0) ? uni(a.coord[j]) : 0;  // coordinates of the current key tile
   int t = 0, tn = 0;  // this split's current / next tile skims (tiered instance)
   if constexpr (TIER) {
     t = (j >= 0) ? uni(sk.t0[grp] != 0 ? 1 : 0) : 0;
@@ -1093,32 +1139,35 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     const int pnn = 2 * (i + 2) + grp;
     const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;
     const int cn_v = (jn >= 0) ? a.ext[jn] : 0;
+    const int ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
     int tnn_v = 0;
     if constexpr (TIER) tnn_v = (pnn < nkeys) ? (sk.t0[pnn] != 0 ? 1 : 0) : 0;
     const TileExtent ext = unpack_extent(code);
+    const int dist = TOKR ? window_dist(cc, qc) : 0;
     if (j >= 0) {
       fetch(j, t, 1, 1);
       const f32x16 s0 = scores(t, 0);
-      softmax_pv_half<D, true>(st, s0, region + KH, 0, lane, ext, a.c2);
+      softmax_pv_half<D, true, TOKR>(st, s0, region + KH, 0, lane, ext, a.c2, dist);
     }
     wait_dma();
     lds_barrier();
     if (jn >= 0) fetch(jn, tn, 0, 0);
     if (j >= 0) {
       const f32x16 s1 = scores(t, 1);
-      softmax_pv_half<D, true>(st, s1, region + BUF + KH, 1, lane, ext, a.c2);
+      softmax_pv_half<D, true, TOKR>(st, s1, region + BUF + KH, 1, lane, ext, a.c2, dist);
     }
     wait_dma();
     lds_barrier();
     j = jn;
     code = uni(cn_v);
+    cc = uni(ccn_v);
     jn = uni(jnn_v);
     t = tn;
     tn = uni(tnn_v);
   }
 }
 
-template <int D, bool TIER>
+template <int D, bool TIER, bool TOKR>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_unit;
@@ -1201,10 +1250,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
       load_q4<D>(st, args.q4 + (qrow0 + q) * Cfg4<D>::kRowBytes,
                  args.q4s + (qrow0 + q) * Cfg4<D>::kC4, h);
     }
+    int qc = 0;  // packed coordinates of this wave's query tile (token-window instance)
+    if constexpr (TOKR) {
+      // this lane's query token and its own radius: 255 (no limit) for routed
+      // rows and padded slots, whose outputs are not windowed or are dropped
+      qc = uni(args.coord[row - (int)bh * nT]);
+      const int qs = 32 * half + q;
+      const int t = 4 * (qc & 1023) + (qs >> 4);
+      const int hh = 4 * ((qc >> 10) & 1023) + ((qs >> 2) & 3);
+      const int w = 4 * ((qc >> 20) & 1023) + (qs & 3);
+      int rl = 255;
+      if (!uni(args.routed[row]) && t < args.T && hh < args.H && w < args.W) {
+        const int64_t n = ((int64_t)t * args.H + hh) * args.W + w;
+        rl = min((int)args.tok_r[bh * ((int64_t)args.T * args.H * args.W) + n], args.r_max);
+      }
+      st.rl = rl;
+    }
     if (g_mode)
-      run_steps_g<D, TIER>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, qp, grp);
+      run_steps_g<D, TIER, TOKR>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, qp,
+                                 grp, qc);
     else
-      run_steps_s<D, TIER>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, grp, qp);
+      run_steps_s<D, TIER, TOKR>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, grp,
+                                 qp, qc);
 
     // S units: merge the two key splits (waves 2,3 -> waves 0,1) through LDS.
     if (!g_mode) {
@@ -1316,7 +1383,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const Header* hdr, const C
 
 hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const void* v,
                        const int* row_ptr, const int* col_idx, float scale, void* o, float* lse,
-                       int kv_chunk, void* ws, int cus, hipStream_t stream, const SkimInputs* skim) {
+                       int kv_chunk, void* ws, int cus, hipStream_t stream, const SkimInputs* skim,
+                       const TokenWindows* tokw) {
   const Grid g = make_grid(s);
   const AttnLayout L = attn_layout(s, kv_chunk);
   char* w = static_cast<char*>(ws);
@@ -1334,6 +1402,7 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   pa.gbase = reinterpret_cast<int*>(w + L.off_gbase);
   pa.grows = reinterpret_cast<int*>(w + L.off_grows);
   pa.ext = reinterpret_cast<int*>(w + L.off_ext);
+  pa.coord = reinterpret_cast<int*>(w + L.off_coord);
   pa.nh = g.nh;
   pa.nw = g.nw;
   pa.T = s.T;
@@ -1355,6 +1424,10 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   aa.o = static_cast<uint16_t*>(o);
   aa.lse = lse;
   aa.ext = pa.ext;
+  aa.coord = pa.coord;
+  aa.tok_r = tokw ? tokw->token_radius : nullptr;
+  aa.routed = tokw ? tokw->routed : nullptr;
+  aa.r_max = tokw ? tokw->r_max : 0;
   aa.hdr = hdr;
   aa.hdr_mut = hdr;
   aa.units = pa.units;
@@ -1375,28 +1448,35 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   const int grid = (int)std::min<int64_t>(L.max_units, 2LL * cus);
   if (s.head_dim == 128) {
     if (skim)
-      attn_kernel<128, true><<<grid, kThreads, Cfg<128>::kLdsBytes + Cfg4<128>::kLdsBytes, stream>>>(aa);
+      attn_kernel<128, true, false><<<grid, kThreads, Cfg<128>::kLdsBytes + Cfg4<128>::kLdsBytes, stream>>>(aa);
+    else if (tokw)
+      attn_kernel<128, false, true><<<grid, kThreads, Cfg<128>::kLdsBytes, stream>>>(aa);
     else
-      attn_kernel<128, false><<<grid, kThreads, Cfg<128>::kLdsBytes, stream>>>(aa);
+      attn_kernel<128, false, false><<<grid, kThreads, Cfg<128>::kLdsBytes, stream>>>(aa);
     combine_kernel<128><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
   } else {
     if (skim)
-      attn_kernel<64, true><<<grid, kThreads, Cfg<64>::kLdsBytes + Cfg4<64>::kLdsBytes, stream>>>(aa);
+      attn_kernel<64, true, false><<<grid, kThreads, Cfg<64>::kLdsBytes + Cfg4<64>::kLdsBytes, stream>>>(aa);
+    else if (tokw)
+      attn_kernel<64, false, true><<<grid, kThreads, Cfg<64>::kLdsBytes, stream>>>(aa);
     else
-      attn_kernel<64, false><<<grid, kThreads, Cfg<64>::kLdsBytes, stream>>>(aa);
+      attn_kernel<64, false, false><<<grid, kThreads, Cfg<64>::kLdsBytes, stream>>>(aa);
     combine_kernel<64><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
   }
   return hipGetLastError();
 }
 
 hipError_t attn_set_lds_limits() {
-  const void* fns[4] = {reinterpret_cast<const void*>(attn_kernel<128, false>),
-                        reinterpret_cast<const void*>(attn_kernel<128, true>),
-                        reinterpret_cast<const void*>(attn_kernel<64, false>),
-                        reinterpret_cast<const void*>(attn_kernel<64, true>)};
-  const int lds[4] = {Cfg<128>::kLdsBytes, Cfg<128>::kLdsBytes + Cfg4<128>::kLdsBytes,
-                      Cfg<64>::kLdsBytes, Cfg<64>::kLdsBytes + Cfg4<64>::kLdsBytes};
-  for (int i = 0; i < 4; ++i) {
+  const void* fns[6] = {reinterpret_cast<const void*>(attn_kernel<128, false, false>),
+                        reinterpret_cast<const void*>(attn_kernel<128, true, false>),
+                        reinterpret_cast<const void*>(attn_kernel<128, false, true>),
+                        reinterpret_cast<const void*>(attn_kernel<64, false, false>),
+                        reinterpret_cast<const void*>(attn_kernel<64, true, false>),
+                        reinterpret_cast<const void*>(attn_kernel<64, false, true>)};
+  const int lds[6] = {Cfg<128>::kLdsBytes, Cfg<128>::kLdsBytes + Cfg4<128>::kLdsBytes,
+                      Cfg<128>::kLdsBytes, Cfg<64>::kLdsBytes,
+                      Cfg<64>::kLdsBytes + Cfg4<64>::kLdsBytes, Cfg<64>::kLdsBytes};
+  for (int i = 0; i < 6; ++i) {
     const hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
     if (e != hipSuccess) return e;
   }

@@ -47,7 +47,7 @@ __device__ __forceinline__ uint64_t tile_valid_mask(int tau, int nh, int nw, int
 struct AttnLayout {
   int64_t rows, bh, max_units, max_slots;
   size_t off_cbase, off_gbase, off_grows, off_units, off_comb, off_po, off_pml, off_ext,
-      total;
+      off_coord, total;
 };
 
 // Launchers (one per source file); each returns the launch status.
@@ -73,10 +73,17 @@ struct SkimInputs {
   const void* k4_scales;
   const uint8_t* tier;
 };
+// Inputs of exact per-token windows (token radii in raster order, the routed
+// flag of every query tile, and the radius clamp).
+struct TokenWindows {
+  const uint8_t* token_radius;
+  const uint8_t* routed;
+  int r_max;
+};
 hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const void* v,
                        const int* row_ptr, const int* col_idx, float scale, void* o, float* lse,
                        int kv_chunk, void* ws, int cus, hipStream_t stream,
-                       const SkimInputs* skim = nullptr);
+                       const SkimInputs* skim = nullptr, const TokenWindows* tokw = nullptr);
 hipError_t launch_quantize_mxfp4(const vsa_shape& s, const void* x_tiled, void* codes,
                                  void* scales, hipStream_t stream);
 hipError_t attn_set_lds_limits();

@@ -261,6 +261,38 @@ vsa_status vsa_attn_fwd_tiered(const vsa_shape* s, const void* q_t, const void* 
                                void* o_t, float* lse_t, int32_t kv_chunk, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ exact per-token windows
+ * "Token Radius Attention for Efficient Video Generation", pipeline steps 2
+ * and 3: every query token has its own radius, and the radii become block
+ * masks.  The block mask of a tile (vsa_build_mask on
+ * vsa_tile_radius_from_tokens) uses the largest radius among its tokens, a
+ * superset of each token's window.
+ *
+ * vsa_attn_fwd_token_window: vsa_attn_fwd on that CSR, with each query token
+ * attending only the kept key tiles that lie inside the window of its own
+ * radius r = min(token_radius, r_max) around its tile (|dt| <= r and
+ * max(|dh|, |dw|) <= r - |dt| in tile coordinates); the query tiles that the
+ * mask builder routed attend every kept key tile.  Every token's own tile
+ * is in its window, so no valid query is left without keys.
+ *   q_t, k_t, v_t, row_ptr, col_idx, scale, o_t, lse_t, kv_chunk, ws,
+ *   ws_bytes: as vsa_attn_fwd (the same workspace size).  The CSR must be
+ *            the mask builder's for tile radii >= each token's radius (e.g.
+ *            vsa_tile_radius_from_tokens of token_radius) and the same r_max:
+ *            keys outside the CSR are never attended.
+ *   routed   uint8 [B][heads][nT]: the mask builder's routed flags.
+ *   token_radius uint8 [B][heads][N], N = T*H*W, raster order.
+ *   r_max    0 <= r_max <= 255, the clamp the mask builder applied.
+ * Errors: as vsa_attn_fwd, plus INVALID_ARG for a NULL routed or
+ * token_radius or an r_max outside [0, 255], and UNSUPPORTED for grids of
+ * 1024 or more tiles along t, h or w.
+ */
+vsa_status vsa_attn_fwd_token_window(const vsa_shape* s, const void* q_t, const void* k_t,
+                                     const void* v_t, const int32_t* row_ptr,
+                                     const int32_t* col_idx, const uint8_t* routed,
+                                     const uint8_t* token_radius, int32_t r_max, float scale,
+                                     void* o_t, float* lse_t, int32_t kv_chunk, void* ws,
+                                     size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
