@@ -140,6 +140,75 @@ def token_level_calls(w, sh, dev, stream, reps):
     return out
 
 
+def token_windows(w, sh, dev, stream, reps, q_t, k_t, v_t, ws, o_t, kv_chunk, kcount):
+    """Exact per-token windows at the workload's size, outside the step: token
+    radii from the token budgets (budget -> radius), the mask from their tile
+    maxima and the tiles' largest token scores, then the attention call that
+    windows each query token by its own radius, beside the block-mask call on
+    the same CSR.  Both do the same tile-pair work; the windowed call masks
+    the (query token, key tile) pairs outside the token's own window."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_19_amd as vsa
+    import workloads as wl
+    r_max = max(w.radius_set)
+    budget, score = wl.token_inputs(w)
+    rad = vsa.budget_to_radius(torch.from_numpy(budget).to(dev), sh, r_max)
+    tr = vsa.tile_radius_from_tokens(rad, sh)
+    ts = vsa.tile_score_from_tokens(torch.from_numpy(score).to(dev), sh)
+    rp, ci, routed = vsa.build_mask(tr, ts, sh, kcount, r_max)
+    torch.cuda.synchronize()
+    nnz = int(rp[-1].item())
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_w = timed(lambda: vsa.attn_fwd_token_window(q_t, k_t, v_t, rp, ci, routed, rad, sh, r_max,
+                                                   w.scale, kv_chunk, out=o_t, workspace=ws,
+                                                   with_lse=False))
+    ms_b = timed(lambda: vsa.attn_fwd(q_t, k_t, v_t, rp, ci, sh, w.scale, kv_chunk, out=o_t,
+                                      workspace=ws, with_lse=False))
+    # share of (query token, kept key tile) pairs outside the token's own
+    # window, over every 16th local row (host count)
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:nnz].cpu().numpy().astype(np.int64)
+    rad_h = rad.cpu().numpy()
+    routed_h = routed.cpu().numpy().reshape(-1)
+    a_, b_, c_ = w.grid_cells
+    coords = np.stack(np.unravel_index(np.arange(w.n_cells), (a_, b_, c_)), axis=1)
+    lt, lh, lw = np.unravel_index(np.arange(64), (4, 4, 4))
+    out_pairs = all_pairs = 0
+    for row in range(0, len(rp_h) - 1, 16):
+        if routed_h[row]:
+            continue
+        h, a = divmod(row, w.n_cells)
+        t0, h0, w0 = 4 * coords[a]
+        tok = (t0 + lt, h0 + lh, w0 + lw)
+        ok = (tok[0] < w.T) & (tok[1] < w.H) & (tok[2] < w.W)
+        n = ((tok[0] * w.H + tok[1]) * w.W + tok[2])[ok]
+        d = np.abs(coords[ci_h[rp_h[row]:rp_h[row + 1]]] - coords[a])
+        dist = d[:, 0] + np.maximum(d[:, 1], d[:, 2])
+        r = np.minimum(rad_h[0, h, n].astype(np.int64), r_max)
+        all_pairs += r.size * dist.size
+        out_pairs += int((dist[None, :] > r[:, None]).sum())
+    flops = nnz * 4.0 * 64 * 64 * w.D
+    return {"r_max": r_max, "retained_tile_pairs": nnz,
+            "windowed_out_share_of_local_pairs": round(out_pairs / max(all_pairs, 1), 4),
+            "attn_token_window": {"ms": round(ms_w, 4),
+                                  "TFLOP/s": round(flops / (ms_w * 1e-3) / 1e12, 2)},
+            "attn_block_mask_same_csr": {"ms": round(ms_b, 4),
+                                         "TFLOP/s": round(flops / (ms_b * 1e-3) / 1e12, 2)}}
+
+
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 MFMA (the skim tier's score products)
 
 
@@ -296,6 +365,8 @@ def main():
         "attn_valid_token_tflops": round(valid_flops / (attn_ms * 1e-3) / 1e12, 2),
     }
     line["token_level_calls"] = token_level_calls(w, sh, dev, stream, args.steps)
+    line["token_windows"] = token_windows(w, sh, dev, stream, args.steps, q_t, k_t, v_t, ws, o_t,
+                                          args.kv_chunk, kcount)
     line["skim_tier"] = skim_tier(w, sh, dev, stream, args.steps, q_t, k_t, v_t, mbuf[0], mbuf[1],
                                   nnz, ws, o_t, attn_ms, args.kv_chunk)
     if args.cpu_seconds > 0:

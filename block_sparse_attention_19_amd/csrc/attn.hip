@@ -790,15 +790,10 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
       s[r] = ok ? s[r] : -INFINITY;
     }
   }
-  if constexpr (TOKR) {
-    // exact per-token windows: this lane's query attends the key tile only if
-    // the tile lies inside the window of the query's own radius
-    if (!__all(st.rl >= dist)) {
-      const bool in = st.rl >= dist;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = in ? s[r] : -INFINITY;
-    }
-  }
+  // exact per-token windows: this lane's query attends the key tile only if
+  // the tile lies inside the window of the query's own radius; otherwise its
+  // tile maximum is -inf (no rescale) and its exp offset -inf (P = 0)
+  const bool in = !TOKR || st.rl >= dist;
   // This lane's 16 scores decide whether the running max must move: the
   // query's max over both lane halves exceeds m + slack exactly when one
   // half's does, so the halves are combined (a cross-lane swap, which does
@@ -807,6 +802,7 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  if (TOKR && !in) mx = -INFINITY;
   if (__any(mx * c2 > st.m + kRescaleSlack)) {
     const float mc = max_halves(mx) * c2;
     const float mn = fmaxf(st.m, mc);
@@ -819,9 +815,11 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
     st.m = mn;
   }
   // every tile holds at least one valid key, so the running max is finite here;
-  // with per-token windows a lane may not have met an attended tile yet (all
-  // its scores so far -inf): its probabilities are then exp2(-inf) = 0
-  const float mneg = (TOKR && st.m == -INFINITY) ? 0.f : -st.m;
+  // with per-token windows a lane may not have met an attended tile yet (its
+  // running max still -inf, its scores here -inf or outside the window): its
+  // probabilities are then exp2(-inf) = 0
+  float mneg = -st.m;
+  if constexpr (TOKR) mneg = !in ? -INFINITY : (st.m == -INFINITY ? 0.f : -st.m);
   bf16x8 pb[2];
   float pf[16];
 #pragma unroll

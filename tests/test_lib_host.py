@@ -170,3 +170,30 @@ def test_skim_calls_validate_before_launch():
     assert call(chunk=-1) == INVALID
     assert call(wsb=ws - 1) == CAPACITY
     assert vsa.lib().vsa_last_error().decode()
+
+
+def test_token_window_call_validates_before_launch():
+    L = vsa.lib()
+    s = vsa.shape(1, 2, 64, 8, 16, 16)
+    sp = ctypes.byref(s)
+    good = _p(0x10000)
+    ws = vsa.attn_workspace_bytes(s, 0)
+
+    def call(shape=sp, **kw):
+        a = dict(q=good, k=good, v=good, rp=good, ci=good, routed=good, tokr=good, r_max=3,
+                 scale=0.125, o=good, lse=None, chunk=0, ws=good, wsb=ws)
+        a.update(kw)
+        return L.vsa_attn_fwd_token_window(shape, a["q"], a["k"], a["v"], a["rp"], a["ci"],
+                                           a["routed"], a["tokr"], a["r_max"], a["scale"],
+                                           a["o"], a["lse"], a["chunk"], a["ws"], a["wsb"], None)
+    assert call(routed=None) == INVALID
+    assert call(tokr=None) == INVALID
+    assert call(r_max=-1) == INVALID
+    assert call(r_max=256) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(chunk=-1) == INVALID
+    assert call(wsb=ws - 1) == CAPACITY
+    # 1024 tiles along w: the packed tile coordinates hold 10 bits per axis
+    wide = vsa.shape(1, 1, 64, 4, 4, 4096)
+    assert call(shape=ctypes.byref(wide), wsb=vsa.attn_workspace_bytes(wide, 0)) == UNSUPPORTED
+    assert vsa.lib().vsa_last_error().decode()
