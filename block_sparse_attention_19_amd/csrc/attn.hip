@@ -30,8 +30,12 @@
 //     query tile and split its key list over two wave pairs, merged in LDS at
 //     the end.  Long G units are split into key chunks that write fp32
 //     partials (O, running max, sum) merged exactly by a combine kernel.
-//     Units are taken from an atomic counter by a persistent grid (2
-//     workgroups per CU), longest class first.
+//     A persistent grid (2 workgroups per CU) takes the units from 8 queues,
+//     one per XCD, long units first and the local rows in row order.
+//   * Three instances of the kernel: the bf16 forward; the skim tier (the
+//     scores of chosen tile pairs from MXFP4 Q and K by scaled MFMA); and
+//     exact per-token windows (each lane's query attends only the listed key
+//     tiles inside the window of its own radius).
 #include "vsa_common.h"
 
 #include <limits.h>
