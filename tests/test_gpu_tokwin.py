@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # collected on CPU hosts only to be deselecte
 
 
 def _run(w, q, k, v, tok_r, scores, kcount, r_max, kv_chunk=0):
-    sh = vsa.shape(1, w.heads, w.D, w.T, w.H, w.W)
+    sh = vsa.shape(q.shape[0], w.heads, w.D, w.T, w.H, w.W)
     q_t = vsa.tile_permute(bf16_to_dev(q), sh, vsa.LAYOUT_TOKEN_MAJOR)
     k_t = vsa.tile_permute(bf16_to_dev(k), sh, vsa.LAYOUT_TOKEN_MAJOR)
     v_t = vsa.tile_permute(bf16_to_dev(v), sh, vsa.LAYOUT_FEATURE_MAJOR)
@@ -69,6 +69,21 @@ def test_token_window_full_small(T, H, W, heads, D, rhi, r_max, kset, kv_chunk):
         ref, lse = vo.token_window_attention(q, k, v, tok_r, s, kcount, r_max, T, H, W, w.scale)
         assert_close(f64_of(out["o"]), ref, "O")
         _check_lse(out, lse, T, H, W, heads)
+
+
+def test_token_window_batch2():
+    """Two batch entries with different inputs, token radii and scores."""
+    T, H, W, heads, D = 9, 10, 11, 2, 128
+    ws = [wl.custom(T, H, W, heads, D, cid=c) for c in (422, 423)]
+    draws = [wl.qkv(w) + wl.radii_scores(w) for w in ws]
+    q, k, v, _, s = (np.concatenate([d[i] for d in draws], axis=0) for i in range(5))
+    rng = np.random.default_rng(424)
+    tok_r = rng.integers(0, 4, size=(2, heads, T * H * W)).astype(np.uint8)
+    for kcount in (0, 3):
+        say(f"token windows batch=2 T={T} H={H} W={W} heads={heads} D={D} k={kcount}")
+        out = _run(ws[0], q, k, v, tok_r, s, kcount, 3)
+        ref, lse = vo.token_window_attention(q, k, v, tok_r, s, kcount, 3, T, H, W, ws[0].scale)
+        assert_close(f64_of(out["o"]), ref, f"O batch=2 k={kcount}")
 
 
 @pytest.mark.parametrize("D", [64, 128])
