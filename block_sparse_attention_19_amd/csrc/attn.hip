@@ -90,10 +90,11 @@ constexpr int kQueueChunk = 16;
 
 struct Header {
   int32_t n_units;
-  int32_t counter;
+  int32_t pad1;
   int32_t n_comb;
-  int32_t chunks_g;
-  int32_t overflow;
+  int32_t chunks_g;    // key chunks per G unit (for inspection; no kernel reads it)
+  int32_t overflow;    // 1: the plan did not fit the workspace and no unit was written
+                       // (cannot happen for a workspace of the size the entry points demand)
   int32_t n_head;      // units [0, n_head): front S and G units, dealt in chunks
   int32_t rest_span;   // units past n_head: queue x owns n_head + [x, x + 1) * rest_span
   int32_t pad0;
@@ -443,7 +444,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       p.hdr->n_units = 0;
       p.hdr->n_comb = 0;
       p.hdr->overflow = 1;
-      p.hdr->counter = 0;
       p.hdr->n_head = 0;
       p.hdr->rest_span = 0;
       for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = p.hdr->queue_rest[x] = 0;
@@ -576,7 +576,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     p.hdr->n_comb = (int)n_comb;
     p.hdr->chunks_g = sg;
     p.hdr->overflow = 0;
-    p.hdr->counter = 0;
     p.hdr->n_head = nFront + ngu;
     p.hdr->rest_span = ((int)n_units - (nFront + ngu) + kQueues - 1) / kQueues;
     for (int x = 0; x < kQueues; ++x) p.hdr->queue[x] = p.hdr->queue_rest[x] = 0;
