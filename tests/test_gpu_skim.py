@@ -166,6 +166,25 @@ def test_attention_tiered_full_small(T, H, W, heads, D, rset, kcount, p):
     assert d.max() <= LSE_ABS
 
 
+def test_attention_tiered_batch2():
+    """Two batch entries with different inputs, radii, scores and tiers."""
+    T, H, W, heads, D = 9, 10, 11, 2, 128
+    ws = [wl.custom(T, H, W, heads, D, radius_set=(0, 1, 2), cid=c) for c in (425, 426)]
+    draws = [wl.qkv(w) + wl.radii_scores(w) for w in ws]
+    q, k, v, r, s = (np.concatenate([d[i] for d in draws], axis=0) for i in range(5))
+    w2 = ws[0].__class__(**{**ws[0].__dict__, "batch": 2})
+    kcount = 3
+    say(f"tiered batch=2 T={T} H={H} W={W} heads={heads} D={D} k={kcount}")
+    sh, q_t, k_t, v_t, rp, ci = _prepare(w2, q, k, v, r, s, kcount)
+    tier = wl.tiers(w2, int(rp[-1].item()), 0.5)
+    o, o_t, lse = _tiered(w2, sh, q_t, k_t, v_t, rp, ci, tier)
+    keep, skim, _ = _oracle_skim(w2, r, s, kcount, tier)
+    O, _ = _oracle_tiered(w2, q, k, v, keep, skim)
+    got = f64_of(o)                                                 # [2, N, heads, D]
+    assert_close(np.stack([got[b, :, h] for b in range(2) for h in range(heads)]), np.stack(O),
+                 "O tiered batch=2")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_attention_tiered_all_refine_is_untiered(D):
     """Every tier 0: the tiered instance runs the bf16 products only, so its
