@@ -85,8 +85,9 @@ struct Comb {
 // one or two heads at a time, which walk the same key tiles in the same order
 // and share them through its L2 (dealing the head in chunks of 16 units made
 // each XCD stream every head: 1.2-1.6x the L2 misses of the whole call, at the
-// same speed).  In the rest (local rows, in row order) the units running at
-// once on an XCD are neighbouring query tiles whose key windows overlap.
+// same speed).  In the rest (local rows, in the order of RowOrder) the units
+// running at once on an XCD are neighbouring query tiles whose key windows
+// overlap.
 constexpr int kQueues = 8;
 
 struct Header {
@@ -202,6 +203,7 @@ struct PlanArgs {
   const int* row_ptr;
   int bh, nT, kv_chunk, target;
   int nh, nw, T, H, W;
+  int blk_h, blk_w;  // spatial block of the row order (see RowOrder)
   int64_t max_units, max_slots;
   Header* hdr;
   int *cbase, *gbase, *grows, *ext, *coord;
@@ -223,13 +225,62 @@ __device__ __forceinline__ int plan_row(int c0, int j) {
   return c0 + ((int)(threadIdx.x >> 6) << 9) + (j << 6) + (int)(threadIdx.x & 63);
 }
 
+// The order in which the plan takes the rows of one (batch, head), and so the
+// order of the local-row units: the tile grid is cut into spatial blocks of
+// blk_h x blk_w tiles (columns of blocks along w outermost, then blocks along
+// h), and each block is taken whole, time slice by time slice, row-major
+// inside a slice.  Units running at once on an XCD then hold query tiles of
+// one narrow spatial block at a few neighbouring times, whose windows share
+// more key tiles in its L2 than whole rows of the grid do (an LRU model of the
+// L2 and measurement both favour blocks of at most 8 x 7 tiles).  Position
+// `pos` of the order is tile tile(pos), and pos(tau) is its inverse: a
+// bijection of [0, nT).  Grids of up to kOrderLds tiles keep the order as a
+// table in LDS, larger ones evaluate tile(pos) per row.
+constexpr int kOrderBlkH = 8, kOrderBlkW = 7;
+constexpr int kOrderLds = 8192;
+struct RowOrder {
+  int nT, nt, nh, nw, blk_h, blk_w;
+  __device__ __forceinline__ int pos(int tau) const {
+    const int tt = tau / (nh * nw);
+    const int rem = tau - tt * (nh * nw);
+    const int th = rem / nw, tw = rem - th * nw;
+    const int wb = tw / blk_w, hb = th / blk_h;
+    const int wl = min(blk_w, nw - wb * blk_w), hl = min(blk_h, nh - hb * blk_h);
+    return wb * (nt * nh * blk_w) + hb * (nt * blk_h * wl) + (tt * hl + (th - hb * blk_h)) * wl +
+           (tw - wb * blk_w);
+  }
+  __device__ __forceinline__ int tile(int pos) const {
+    const int col = nt * nh * blk_w;  // positions in a full column of blocks
+    const int wb = pos / col;         // (only the last column can be narrower)
+    int rem = pos - wb * col;
+    const int wl = min(blk_w, nw - wb * blk_w);
+    const int cell = nt * blk_h * wl;  // positions in a full block of the column
+    const int hb = rem / cell;
+    rem -= hb * cell;
+    const int hl = min(blk_h, nh - hb * blk_h);
+    const int tt = rem / (hl * wl);
+    rem -= tt * (hl * wl);
+    const int th = hb * blk_h + rem / wl, tw = wb * blk_w + rem % wl;
+    return (tt * nh + th) * nw + tw;
+  }
+  // row index of iteration index i (same (batch, head): i / nT); `table`
+  // holds tile(pos) for every pos when it is not null
+  __device__ __forceinline__ int row(int i, const int* table) const {
+    const int b = i / nT;
+    const int p = i - b * nT;
+    return b * nT + (table ? table[p] : tile(p));
+  }
+};
+
 // Lengths of this thread's rows of the block at c0 (-1 past the last row).
 __device__ __forceinline__ void load_lengths(const int* row_ptr, int rows, int c0,
+                                             const RowOrder& ord, const int* table,
                                              int (&len)[kPlanSeg]) {
   int a[kPlanSeg], b[kPlanSeg];
 #pragma unroll
   for (int j = 0; j < kPlanSeg; ++j) {
-    const int r = min(plan_row(c0, j), rows);
+    const int i = plan_row(c0, j);
+    const int r = (i < rows) ? ord.row(i, table) : rows;
     a[j] = row_ptr[r];
     b[j] = row_ptr[min(r + 1, rows)];
   }
@@ -334,6 +385,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   const int nT = p.nT;  // >= 1
   const int t = threadIdx.x;
   const int rows = p.bh * nT;
+  const RowOrder ord = {nT, nT / (p.nh * p.nw), p.nh, p.nw, p.blk_h, p.blk_w};
   constexpr bool chunked = CHUNKED;
   const int chunk_s = p.kv_chunk;
   // S chunks of a row of `len` keys, and the key count of chunk c
@@ -351,11 +403,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     return f;
   };
 
+  __shared__ int s_order[kOrderLds];
+  const int* table = (nT <= kOrderLds) ? s_order : nullptr;
   for (int tau = t; tau < nT; tau += kPlanThreads) {
     p.ext[tau] = pack_extent(tau, p.nh, p.nw, p.T, p.H, p.W);
     p.coord[tau] = pack_coord(tau, p.nh, p.nw);
+    if (table) s_order[ord.pos(tau)] = tau;
   }
   if (t == 0) s_front = 0;
+  __syncthreads();
 
   // pass 1: cbase[b] = complete rows before (b, h) (a scan of the complete-row
   // flags in row order), and the S totals of the incomplete rows.  With a
@@ -365,7 +421,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   int a_units = 0, a_front = 0, a_slots = 0, a_comb = 0;
   int carry_c = 0;
   for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
-    load_lengths(p.row_ptr, rows, c0, len);
+    load_lengths(p.row_ptr, rows, c0, ord, table, len);
     int before[1][kPlanSeg];
 #pragma unroll
     for (int j = 0; j < kPlanSeg; ++j) before[0][j] = (len[j] == nT);
@@ -374,9 +430,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
 #pragma unroll
     for (int j = 0; j < kPlanSeg; ++j) {
       if (len[j] < 0) continue;
-      const int r = plan_row(c0, j);
-      const int b = r / nT;
-      if (r == b * nT) p.cbase[b] = carry_c + before[0][j];
+      const int i = plan_row(c0, j);  // iteration index; its row is in (b, h) = i / nT
+      const int b = i / nT;
+      if (i == b * nT) p.cbase[b] = carry_c + before[0][j];
       if (len[j] != nT) {
         const int n = n_chunks(len[j]);
         a_units += n;
@@ -456,9 +512,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
 
   // Unit order: S units of at least half a full row first (complete rows left
   // over from the pairing), so that no unit as long as a G unit starts late;
-  // then the G units; then the other S units in row order, so that
-  // neighbouring query tiles, whose key windows overlap, run close in time on
-  // one XCD and share its L2.
+  // then the G units; then the other S units in the plan's row order (spatial
+  // blocks, RowOrder), so that neighbouring query tiles, whose key windows
+  // overlap, run close in time on one XCD and share its L2.
   const int ngu = (int)nGU, gsl = (int)gslots;
   const int rest_base = nFront + ngu;
   const int comb_base = (sg > 1) ? 2 * NG : 0;
@@ -467,7 +523,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   int carry_rest = 0, carry_slot = 0, carry_comb = 0;
   carry_c = 0;
   for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
-    if (!one_block) load_lengths(p.row_ptr, rows, c0, len);
+    if (!one_block) load_lengths(p.row_ptr, rows, c0, ord, table, len);
     int before[1][kPlanSeg];
 #pragma unroll
     for (int j = 0; j < kPlanSeg; ++j) before[0][j] = (len[j] == nT);
@@ -482,10 +538,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
       nS[j] = 0;
 #pragma unroll
       for (int k = 0; k < NC; ++k) cnt[k][j] = 0;
-      const int r = plan_row(c0, j);
-      const int b = min(r, rows - 1) / nT;
+      const int i = plan_row(c0, j);
+      const int b = min(i, rows - 1) / nT;
       const int cb_r = p.cbase[b], cnt_r = p.cbase[b + 1] - cb_r, gb_r = p.gbase[b];
       if (len[j] < 0) continue;
+      const int r = ord.row(i, table);
       bool g_member = false;
       if (len[j] == nT) {
         const int jj = carry_c + before[0][j] - cb_r;  // index among the complete rows of (b, h)
@@ -512,7 +569,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     for (int j = 0; j < kPlanSeg; ++j) {
       const int n = nS[j];
       if (n == 0) continue;
-      const int r = plan_row(c0, j);
+      const int r = ord.row(plan_row(c0, j), table);
       int pos_rest = carry_rest + cnt[0][j];
       int slot0 = -1;
       if constexpr (CHUNKED) slot0 = gsl + carry_slot + cnt[1][j];
@@ -1412,6 +1469,10 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   pa.T = s.T;
   pa.H = s.H;
   pa.W = s.W;
+  // the smallest even cut of the tile grid into blocks of at most
+  // kOrderBlkH x kOrderBlkW tiles
+  pa.blk_h = (g.nh + (g.nh + kOrderBlkH - 1) / kOrderBlkH - 1) / ((g.nh + kOrderBlkH - 1) / kOrderBlkH);
+  pa.blk_w = (g.nw + (g.nw + kOrderBlkW - 1) / kOrderBlkW - 1) / ((g.nw + kOrderBlkW - 1) / kOrderBlkW);
   pa.units = reinterpret_cast<Unit*>(w + L.off_units);
   pa.comb = reinterpret_cast<Comb*>(w + L.off_comb);
   if (kv_chunk > 0)

@@ -25,7 +25,8 @@ def _shape(w):
     return vsa.shape(w.batch, w.heads, w.D, w.T, w.H, w.W)
 
 
-def _run_all(w, q, k, v, r, s, kcount, kv_chunk=0, r_max=None):
+def _run_all(w, q, k, v, r, s, kcount, kv_chunk=0, r_max=None, nan_out=False):
+    """nan_out: the tiled output starts as NaN, so a row the call never writes shows."""
     sh = _shape(w)
     qd, kd, vd = bf16_to_dev(q), bf16_to_dev(k), bf16_to_dev(v)
     q_t = vsa.tile_permute(qd, sh, vsa.LAYOUT_TOKEN_MAJOR)
@@ -33,7 +34,8 @@ def _run_all(w, q, k, v, r, s, kcount, kv_chunk=0, r_max=None):
     v_t = vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR)
     rp, ci, routed = vsa.build_mask(torch.from_numpy(r).to(dev()), torch.from_numpy(s).to(dev()),
                                     sh, kcount, r_max if r_max is not None else max(w.radius_set))
-    o_t, lse = vsa.attn_fwd(q_t, k_t, v_t, rp, ci, sh, w.scale, kv_chunk)
+    o_init = torch.full_like(q_t, float("nan")) if nan_out else None
+    o_t, lse = vsa.attn_fwd(q_t, k_t, v_t, rp, ci, sh, w.scale, kv_chunk, out=o_init)
     o = vsa.tile_unpermute(o_t, sh)
     torch.cuda.synchronize()
     return dict(q_t=q_t, k_t=k_t, v_t=v_t, rp=rp, ci=ci, routed=routed, o_t=o_t, lse=lse, o=o)
@@ -126,6 +128,9 @@ SMALL = [  # T, H, W, heads, D, radius set, routed counts
     (13, 9, 17, 2, 128, (1, 2, 3, 4), (0, 5, 60)),
     (1, 1, 1, 1, 64, (0,), (0, 1)),
     (12, 8, 8, 2, 128, (0,), (0,)),
+    # tile grids cut unevenly into the plan's spatial blocks (10 x 9 and 6 x 8 tiles)
+    (4, 40, 36, 1, 64, (1, 2, 3), (0, 9)),
+    (8, 24, 32, 1, 64, (1, 2), (0, 5)),
 ]
 
 
@@ -240,6 +245,24 @@ def test_attention_plan_block_boundary(heads, kv_chunk):
     r, s = wl.radii_scores(w)
     out = _run_all(w, q, k, v, r, s, kcount, kv_chunk=kv_chunk)
     _check_sampled(w, q, k, v, r, s, kcount, out, heads=sorted({0, 31, heads - 1}), seed=heads)
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_attention_plan_order_without_lds_table():
+    """The plan keeps its spatial-block row order as an LDS table for grids of
+    up to 8192 tiles; this grid has 1 x 1 x 8200 tiles, so the order is
+    evaluated per row.  Every valid output row is written (the output starts as
+    NaN), and sampled rows match the oracle."""
+    T, H, W, D = 4, 4, 4 * 8200, 64
+    w = wl.custom(T, H, W, 1, D, radius_set=(1, 2, 3), cid=414)
+    kcount = 3
+    say(f"attention plan order T={T} H={H} W={W} k={kcount}")
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    out = _run_all(w, q, k, v, r, s, kcount, nan_out=True)
+    assert torch.isfinite(out["o"].float()).all().item(), "an output row was not written"
+    _check_sampled(w, q, k, v, r, s, kcount, out, heads=[0], seed=414)
     del out
     torch.cuda.empty_cache()
 
