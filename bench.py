@@ -1,9 +1,13 @@
 """Benchmark of one block-sparse video attention call on one MI355X.
 
 A step is the whole path over one batch of synthetic, HBM-resident input:
-tile permute of Q, K (token-major) and V (feature-major), CSR mask build from
-per-tile radii and routing scores, block-sparse attention forward (plan,
-flash kernel, split combine) and the unpermute of O.  Default workload: the
+tile permute of K (token-major) and V (feature-major), CSR mask build from
+per-tile radii and routing scores, and the block-sparse attention forward
+(plan, flash kernel, split combine) of vsa_attn_fwd_raster, which gathers
+each query tile's rows from the raster Q and writes every token's output row
+to the raster O (the Q permute and the O unpermute, fused).  The same path
+with the Q permute and the O unpermute as kernels of their own (vsa_attn_fwd
+on tile-major Q and O) is timed beside it (``step_unfused_ms``).  Default workload: the
 Wan2.1-1.3B 480p-shaped call, 21x30x52 latent grid (32760 tokens), 12 heads,
 head_dim 128, radii in {1, 2, 3}, 20% of query tiles routed dense.
 
@@ -290,32 +294,40 @@ def main():
     o_t = torch.empty_like(q_t)
     lse = torch.empty((1, w.heads, nT * 64), dtype=torch.float32, device=dev)
     o = torch.empty_like(qd)
+    lse_r = torch.empty((1, w.heads, w.tokens), dtype=torch.float32, device=dev)
     mbuf = vsa.mask_buffers(sh, kcount, r_max, dev)
     ws = torch.empty(vsa.attn_workspace_bytes(sh, args.kv_chunk), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    stages = ["permute_qkv", "mask", "attn", "unpermute"]
+    stages = ["permute_kv", "mask", "attn"]
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        vsa.tile_permute(qd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=q_t)
         vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=k_t)
         vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR, out=v_t)
         mark(1)
         rp, ci, _ = vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf)
         mark(2)
+        vsa.attn_fwd_raster(qd, k_t, v_t, rp, ci, sh, w.scale, args.kv_chunk, out=o,
+                            workspace=ws, lse_out=lse_r)
+        mark(3)
+
+    def step_unfused():
+        vsa.tile_permute(qd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=q_t)
+        vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=k_t)
+        vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR, out=v_t)
+        rp, ci, _ = vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf)
         vsa.attn_fwd(q_t, k_t, v_t, rp, ci, sh, w.scale, args.kv_chunk, out=o_t, workspace=ws,
                      lse_out=lse)
-        mark(3)
         vsa.tile_unpermute(o_t, sh, out=o)
-        mark(4)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -327,6 +339,24 @@ def main():
     ms_step = t_all0.elapsed_time(t_all1) / args.steps
     per_stage = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
                  for j, n in enumerate(stages)}
+    # the unfused path (tile-major Q and O, permute and unpermute as kernels);
+    # it also leaves the tile-major Q in q_t for the side measurements below
+    u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    u0.record(stream)
+    for _ in range(args.steps):
+        step_unfused()
+    u1.record(stream)
+    torch.cuda.synchronize()
+    ms_unfused = u0.elapsed_time(u1) / args.steps
+    # the tile-major call alone (the reference of the side measurements)
+    rp_, ci_ = mbuf[0], mbuf[1]
+    u0.record(stream)
+    for _ in range(args.steps):
+        vsa.attn_fwd(q_t, k_t, v_t, rp_, ci_, sh, w.scale, args.kv_chunk, out=o_t, workspace=ws,
+                     lse_out=lse)
+    u1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn_tiled = u0.elapsed_time(u1) / args.steps
     nnz = int(mbuf[0][-1].item())
     flops = nnz * 4.0 * 64 * 64 * w.D
     # valid-token flops: each kept pair weighted by valid queries x valid keys
@@ -360,15 +390,17 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_figure(1.0),
-                     "kernel": "vsa_attn_fwd (plan + attn_kernel + combine_kernel)"},
+                     "kernel": "vsa_attn_fwd_raster (plan + attn_kernel + combine_kernel)"},
         "breakdown_ms": {k2: round(v2, 4) for k2, v2 in per_stage.items()},
+        "step_unfused_ms": round(ms_unfused, 4),
+        "attn_tile_major_ms": round(ms_attn_tiled, 4),
         "attn_valid_token_tflops": round(valid_flops / (attn_ms * 1e-3) / 1e12, 2),
     }
     line["token_level_calls"] = token_level_calls(w, sh, dev, stream, args.steps)
     line["token_windows"] = token_windows(w, sh, dev, stream, args.steps, q_t, k_t, v_t, ws, o_t,
                                           args.kv_chunk, kcount)
     line["skim_tier"] = skim_tier(w, sh, dev, stream, args.steps, q_t, k_t, v_t, mbuf[0], mbuf[1],
-                                  nnz, ws, o_t, attn_ms, args.kv_chunk)
+                                  nnz, ws, o_t, ms_attn_tiled, args.kv_chunk)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, r, s, kcount, args.cpu_seconds)
     else:

@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         "vsa_tile_score_from_tokens": (ctypes.c_int, [SP, P, P, P]),
         "vsa_attn_workspace_bytes": (SZ, [SP, I32]),
         "vsa_attn_fwd": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, I32, P, SZ, P]),
+        "vsa_attn_fwd_raster": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, I32, P, SZ, P]),
         "vsa_quantize_mxfp4": (ctypes.c_int, [SP, P, P, P, P]),
         "vsa_attn_fwd_tiered": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, I32, P, SZ, P]),
@@ -274,6 +275,48 @@ def attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: t
                               _ptr(col_idx), scale, _ptr(out), _ptr(lse), kv_chunk,
                               _ptr(workspace), workspace.numel(), _stream(dev)),
            "vsa_attn_fwd")
+    return out, lse
+
+
+def attn_fwd_raster(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: torch.Tensor,
+                    col_idx: torch.Tensor, s: Shape, scale: Optional[float] = None,
+                    kv_chunk: int = 0, with_lse: bool = True, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Raster q [B, N, heads, D], tile-major k_t, feature-major v_t + CSR ->
+    (o bf16 [B, N, heads, D], lse float32 [B, heads, N]): the Q permute and the
+    O unpermute happen inside the call."""
+    q = _require(q, torch.bfloat16, "q")
+    k_t = _require(k_t, torch.bfloat16, "k_t")
+    v_t = _require(v_t, torch.bfloat16, "v_t")
+    row_ptr = _require(row_ptr, torch.int32, "row_ptr")
+    col_idx = _require(col_idx, torch.int32, "col_idx")
+    nT = num_tiles(s)
+    D = s.head_dim
+    N = s.T * s.H * s.W
+    ras = (s.batch, N, s.heads, D)
+    if q.shape != ras:
+        raise ValueError("q must be [B, N, heads, D]")
+    if k_t.shape != (s.batch, s.heads, nT * 64, D) or v_t.shape != (s.batch, s.heads, nT, D, 64):
+        raise ValueError("k_t / v_t shapes do not match the shape")
+    if row_ptr.numel() != s.batch * s.heads * nT + 1:
+        raise ValueError("row_ptr must have B*heads*nT + 1 entries")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty(ras, dtype=torch.bfloat16, device=dev)
+    elif out.shape != ras or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [B, N, heads, D] tensor")
+    lse = lse_out
+    if lse is None and with_lse:
+        lse = torch.empty((s.batch, s.heads, N), dtype=torch.float32, device=dev)
+    ws_bytes = attn_workspace_bytes(s, kv_chunk)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(lib().vsa_attn_fwd_raster(ctypes.byref(s), _ptr(q), _ptr(k_t), _ptr(v_t),
+                                     _ptr(row_ptr), _ptr(col_idx), scale, _ptr(out), _ptr(lse),
+                                     kv_chunk, _ptr(workspace), workspace.numel(), _stream(dev)),
+           "vsa_attn_fwd_raster")
     return out, lse
 
 

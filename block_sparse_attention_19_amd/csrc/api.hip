@@ -257,17 +257,20 @@ size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk) {
   return attn_layout(*s, kv_chunk).total;
 }
 
-vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t, const void* v_t,
-                        const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o_t,
-                        float* lse_t, int32_t kv_chunk, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks shared by the tile-major and the raster forward calls.
+static vsa_status check_attn_args(const vsa_shape* s, const void* q, const char* q_name,
+                                  const void* k_t, const void* v_t, const int32_t* row_ptr,
+                                  const int32_t* col_idx, float scale, const void* o,
+                                  const char* o_name, const float* lse, const char* lse_name,
+                                  int32_t kv_chunk, const void* ws, size_t ws_bytes) {
   VSA_TRY(check_shape(s));
-  VSA_TRY(check_ptr(q_t, 16, "q_t"));
+  VSA_TRY(check_ptr(q, 16, q_name));
   VSA_TRY(check_ptr(k_t, 16, "k_t"));
   VSA_TRY(check_ptr(v_t, 16, "v_t"));
   VSA_TRY(check_ptr(row_ptr, 4, "row_ptr"));
   VSA_TRY(check_ptr(col_idx, 4, "col_idx"));
-  VSA_TRY(check_ptr(o_t, 16, "o_t"));
-  if (lse_t) VSA_TRY(check_ptr(lse_t, 4, "lse_t"));
+  VSA_TRY(check_ptr(o, 16, o_name));
+  if (lse) VSA_TRY(check_ptr(lse, 4, lse_name));
   VSA_TRY(check_ptr(ws, 256, "ws"));
   if (!(scale > 0.f) || scale > 3.0e38f) {
     set_error("scale must be finite and > 0");
@@ -282,10 +285,31 @@ vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t, co
     set_error("attention workspace %zu < %zu bytes", ws_bytes, need);
     return VSA_ERR_CAPACITY;
   }
+  return VSA_OK;
+}
+
+vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t, const void* v_t,
+                        const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o_t,
+                        float* lse_t, int32_t kv_chunk, void* ws, size_t ws_bytes, void* stream) {
+  VSA_TRY(check_attn_args(s, q_t, "q_t", k_t, v_t, row_ptr, col_idx, scale, o_t, "o_t", lse_t,
+                          "lse_t", kv_chunk, ws, ws_bytes));
   int cus = 0;
   VSA_TRY(device_cus(&cus));
   return hip_status(launch_attn(*s, q_t, k_t, v_t, row_ptr, col_idx, scale, o_t, lse_t, kv_chunk,
                                 ws, cus, static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+vsa_status vsa_attn_fwd_raster(const vsa_shape* s, const void* q, const void* k_t, const void* v_t,
+                               const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                               void* o, float* lse, int32_t kv_chunk, void* ws, size_t ws_bytes,
+                               void* stream) {
+  VSA_TRY(check_attn_args(s, q, "q", k_t, v_t, row_ptr, col_idx, scale, o, "o", lse, "lse",
+                          kv_chunk, ws, ws_bytes));
+  int cus = 0;
+  VSA_TRY(device_cus(&cus));
+  return hip_status(launch_attn(*s, q, k_t, v_t, row_ptr, col_idx, scale, o, lse, kv_chunk, ws,
+                                cus, static_cast<hipStream_t>(stream), nullptr, nullptr, true),
                     "attention launch");
 }
 

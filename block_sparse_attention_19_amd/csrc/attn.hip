@@ -644,14 +644,48 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
 
 // -------------------------------------------------------------- attention
 
+// Where the query and the output of a tile slot live.  Tile-major (the
+// permuted layout): row `row` of the CSR, slot s at element ((row * 64) + s) * D,
+// LSE at row * 64 + s.  Raster (the caller's [B][N][Hh][D] layout, LSE
+// [B][Hh][N]): the slot's token (t, h, w) of tile tau = row mod nT, at element
+// ((b * N + n) * Hh + head) * D with n = (t * H + h) * W + w; a padded slot has
+// no token (tok_at returns false and points at token 0; the query row of such
+// a slot is loaded as +0.0 and its output is not written).
+__device__ __forceinline__ bool tok_at(int raster, int heads, int nT, int nh, int nw, int T, int H,
+                                       int W, int row, int s, int D, int64_t& off, int64_t& li) {
+  if (!raster) {
+    li = (int64_t)row * kTileTokens + s;
+    off = li * D;
+    return true;
+  }
+  const int64_t N = (int64_t)T * H * W;
+  const int bh = row / nT, tau = row - bh * nT;
+  const int tw = tau % nw, th = (tau / nw) % nh, tt = tau / (nw * nh);
+  const int t = 4 * tt + (s >> 4), hh = 4 * th + ((s >> 2) & 3), w = 4 * tw + (s & 3);
+  const bool ok = t < T && hh < H && w < W;
+  const int64_t n = ok ? ((int64_t)t * H + hh) * W + w : 0;
+  const int b = bh / heads, h = bh - b * heads;
+  off = (((int64_t)b * N + n) * heads + h) * D;
+  li = (int64_t)bh * N + n;
+  return ok;
+}
+// The same mapping, bundled for the combine kernel.
+struct TokMap {
+  int raster, heads, nT, nh, nw, T, H, W;
+  __device__ __forceinline__ bool at(int row, int s, int D, int64_t& off, int64_t& li) const {
+    return tok_at(raster, heads, nT, nh, nw, T, H, W, row, s, D, off, li);
+  }
+};
+
 struct AttnArgs {
-  const uint16_t* q;   // [BH][nT*64][D]
+  const uint16_t* q;   // [BH][nT*64][D], or raster [B][N][Hh][D] (raster)
   const uint16_t* k;   // [BH][nT*64][D]
   const uint16_t* v;   // [BH][nT][D][64]
   const int* row_ptr;
   const int* col_idx;
-  uint16_t* o;         // [BH][nT*64][D]
-  float* lse;          // [BH][nT*64] or null
+  uint16_t* o;         // [BH][nT*64][D], or raster [B][N][Hh][D] (raster)
+  float* lse;          // [BH][nT*64], or raster [B][Hh][N]; or null
+  int raster, heads;   // raster: q, o and lse in the caller's layout (tok_at)
   const int* ext;      // packed extent per key tile
   const Header* hdr;
   Header* hdr_mut;
@@ -751,8 +785,15 @@ struct WaveState {
 // rows, 8 features per 16-feature k-step (lane half h takes the upper 8).
 template <int D>
 __device__ __forceinline__ void load_q(WaveState<D>& st, const uint16_t* qp) {
+  // qp is null for a padded slot of a raster query: its row is +0.0, as the
+  // tile permute writes it (the wave's rescale decisions see the same scores)
+  if (qp) {
 #pragma unroll
-  for (int t = 0; t < Cfg<D>::kKSteps; ++t) st.qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
+    for (int t = 0; t < Cfg<D>::kKSteps; ++t) st.qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < Cfg<D>::kKSteps; ++t) st.qreg[t] = bf16x8{};
+  }
 }
 
 // Skim tier.  This wave's MXFP4 Q fragments: for k-block m (64 features), the
@@ -1289,7 +1330,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     const int64_t qrow0 = (int64_t)row * kTileTokens + 32 * half;
 
     WaveState<D> st;
-    const uint16_t* qp = args.q + (qrow0 + q) * D + 8 * h;
+    int64_t q_off, q_li;
+    const bool q_ok = tok_at(args.raster, args.heads, nT, args.nh, args.nw, args.T, args.H,
+                             args.W, row, 32 * half + q, D, q_off, q_li);
+    const uint16_t* qp = q_ok ? args.q + q_off + 8 * h : nullptr;
 #pragma unroll
     for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
 #pragma unroll
@@ -1367,9 +1411,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     if (writer) {
       const float lt = sum_halves(st.l);
       const int qi = 32 * half + q;  // query row within the tile
-      if (u.slot < 0) {
+      int64_t o_off, o_li;
+      const bool o_ok = tok_at(args.raster, args.heads, nT, args.nh, args.nw, args.T, args.H,
+                               args.W, row, qi, D, o_off, o_li);
+      if (u.slot < 0 && o_ok) {
         const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-        uint16_t* op = args.o + (qrow0 + q) * D + 4 * h;
+        uint16_t* op = args.o + o_off + 4 * h;
 #pragma unroll
         for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
 #pragma unroll
@@ -1384,8 +1431,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
             *reinterpret_cast<uint2*>(op + 32 * db + 8 * g) = w;
           }
         if (args.lse && h == 0)
-          args.lse[qrow0 + q] = (lt > 0.f) ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
-      } else {
+          args.lse[o_li] = (lt > 0.f) ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
+      } else if (u.slot >= 0) {
         const int64_t slot = u.slot + (g_mode ? grp : 0);
         float* po = args.part_o + slot * kTileTokens * D + (int64_t)qi * D + 4 * h;
 #pragma unroll
@@ -1408,12 +1455,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const Header* hdr, const Comb* comb,
                                                       const float* part_o, const float* part_ml,
-                                                      uint16_t* o, float* lse) {
+                                                      uint16_t* o, float* lse, TokMap map) {
   const int n_comb = hdr->n_comb;
   constexpr int kVec = D / 4;                    // float4 per row
   for (int ci = blockIdx.x; ci < n_comb; ci += gridDim.x) {
     const Comb c = comb[ci];
-    const int64_t orow0 = (int64_t)c.row * kTileTokens;
     for (int i = threadIdx.x; i < kTileTokens * kVec; i += blockDim.x) {
       const int r = i / kVec, v4 = i % kVec;
       float M = -INFINITY;
@@ -1434,8 +1480,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const Header* hdr, const C
       uint2 w2;
       w2.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
       w2.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-      *reinterpret_cast<uint2*>(o + (orow0 + r) * D + 4 * v4) = w2;
-      if (lse && v4 == 0) lse[orow0 + r] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+      int64_t off, li;
+      if (!map.at(c.row, r, D, off, li)) continue;  // a padded slot of a raster output
+      *reinterpret_cast<uint2*>(o + off + 4 * v4) = w2;
+      if (lse && v4 == 0) lse[li] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -1445,7 +1493,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const Header* hdr, const C
 hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const void* v,
                        const int* row_ptr, const int* col_idx, float scale, void* o, float* lse,
                        int kv_chunk, void* ws, int cus, hipStream_t stream, const SkimInputs* skim,
-                       const TokenWindows* tokw) {
+                       const TokenWindows* tokw, bool raster) {
   const Grid g = make_grid(s);
   const AttnLayout L = attn_layout(s, kv_chunk);
   char* w = static_cast<char*>(ws);
@@ -1505,6 +1553,9 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   aa.H = s.H;
   aa.W = s.W;
   aa.c2 = scale * kLog2e;
+  aa.raster = raster ? 1 : 0;
+  aa.heads = s.heads;
+  const TokMap map = {aa.raster, s.heads, g.nT, g.nh, g.nw, s.T, s.H, s.W};
   aa.q4 = skim ? static_cast<const uint8_t*>(skim->q4) : nullptr;
   aa.q4s = skim ? static_cast<const uint8_t*>(skim->q4_scales) : nullptr;
   aa.k4 = skim ? static_cast<const uint8_t*>(skim->k4) : nullptr;
@@ -1518,7 +1569,7 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
       attn_kernel<128, false, true><<<grid, kThreads, Cfg<128>::kLdsBytes, stream>>>(aa);
     else
       attn_kernel<128, false, false><<<grid, kThreads, Cfg<128>::kLdsBytes, stream>>>(aa);
-    combine_kernel<128><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
+    combine_kernel<128><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse, map);
   } else {
     if (skim)
       attn_kernel<64, true, false><<<grid, kThreads, Cfg<64>::kLdsBytes + Cfg4<64>::kLdsBytes, stream>>>(aa);
@@ -1526,7 +1577,7 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
       attn_kernel<64, false, true><<<grid, kThreads, Cfg<64>::kLdsBytes, stream>>>(aa);
     else
       attn_kernel<64, false, false><<<grid, kThreads, Cfg<64>::kLdsBytes, stream>>>(aa);
-    combine_kernel<64><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse);
+    combine_kernel<64><<<std::max(1, 2 * cus), 256, 0, stream>>>(hdr, pa.comb, aa.part_o, aa.part_ml, aa.o, lse, map);
   }
   return hipGetLastError();
 }

@@ -83,7 +83,8 @@ struct TokenWindows {
 hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const void* v,
                        const int* row_ptr, const int* col_idx, float scale, void* o, float* lse,
                        int kv_chunk, void* ws, int cus, hipStream_t stream,
-                       const SkimInputs* skim = nullptr, const TokenWindows* tokw = nullptr);
+                       const SkimInputs* skim = nullptr, const TokenWindows* tokw = nullptr,
+                       bool raster = false);
 hipError_t launch_quantize_mxfp4(const vsa_shape& s, const void* x_tiled, void* codes,
                                  void* scales, hipStream_t stream);
 hipError_t attn_set_lds_limits();

@@ -214,6 +214,28 @@ vsa_status vsa_attn_fwd(const vsa_shape* s, const void* q_t, const void* k_t,
                         float scale, void* o_t, float* lse_t, int32_t kv_chunk,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* vsa_attn_fwd_raster: vsa_attn_fwd with the query read from, and the output
+ * written to, the caller's raster layout, so that the Q permute and the O
+ * unpermute of the pipeline (TRA, step 3: tile-major token layout; the padded
+ * query slots' outputs are discarded) happen inside the call: each query tile
+ * gathers its 64 token rows, and each real token's output row is written in
+ * place.  The arithmetic is that of vsa_attn_fwd, so O and LSE are bitwise
+ * those of vsa_attn_fwd followed by vsa_tile_unpermute (and the same permute
+ * of the LSE).
+ *   q        bf16 [B][N][heads][D] (raster, N = T*H*W), 16-byte aligned.
+ *   k_t, v_t, row_ptr, col_idx, scale, kv_chunk, ws, ws_bytes: as
+ *            vsa_attn_fwd (the same workspace size).
+ *   o        bf16 [B][N][heads][D], every element written; 16-byte aligned.
+ *            Must not overlap q.
+ *   lse      optional fp32 [B][heads][N], natural-log LSE of every token;
+ *            NULL to skip.
+ * Errors: as vsa_attn_fwd.
+ */
+vsa_status vsa_attn_fwd_raster(const vsa_shape* s, const void* q, const void* k_t,
+                               const void* v_t, const int32_t* row_ptr, const int32_t* col_idx,
+                               float scale, void* o, float* lse, int32_t kv_chunk, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* ----------------------------------------------------- low-precision tier
  * "Triage: Skip, Skim, or Refine Attention Tiles in Video Diffusion
  * Transformers" (plain-words summary; "Route by estimated error"): every

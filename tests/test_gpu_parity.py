@@ -267,6 +267,64 @@ def test_attention_plan_order_without_lds_table():
     torch.cuda.empty_cache()
 
 
+RASTER_CASES = [  # T, H, W, heads, D, radius set, routed count, kv_chunk
+    (8, 16, 16, 2, 64, (1, 2, 3), 6, 0),
+    (5, 6, 7, 2, 128, (0, 1, 2), 1, 0),
+    (13, 9, 17, 2, 128, (1, 2, 3, 4), 5, 3),
+    (4, 40, 36, 1, 64, (1, 2, 3), 9, 0),
+    (1, 1, 1, 1, 64, (0,), 0, 0),
+]
+
+
+def _raster(w, q, out, kv_chunk):
+    """The raster call on the caller's Q, with K/V/CSR of `out`; O starts as NaN."""
+    sh = _shape(w)
+    o = torch.full((1, w.T * w.H * w.W, w.heads, w.D), float("nan"), dtype=torch.bfloat16,
+                   device=dev())
+    qd = bf16_to_dev(q)
+    o, lse = vsa.attn_fwd_raster(qd, out["k_t"], out["v_t"], out["rp"], out["ci"], sh, w.scale,
+                                 kv_chunk, out=o)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("T,H,W,heads,D,rset,kcount,kv_chunk", RASTER_CASES)
+def test_attention_raster_matches_tiled(T, H, W, heads, D, rset, kcount, kv_chunk):
+    """vsa_attn_fwd_raster gathers Q from and scatters O (and LSE) to the raster
+    layout inside the call: bitwise the tile-major call followed by the
+    unpermute, every element written (the output starts as NaN), and within
+    tolerance of the oracle."""
+    w = wl.custom(T, H, W, heads, D, radius_set=rset, cid=415)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    say(f"attention raster T={T} H={H} W={W} heads={heads} D={D} k={kcount} kv_chunk={kv_chunk}")
+    out = _run_all(w, q, k, v, r, s, kcount, kv_chunk=kv_chunk)
+    o, lse = _raster(w, q, out, kv_chunk)
+    assert np.array_equal(bits_of(o), bits_of(out["o"])), "raster O differs from unpermuted O"
+    lse_t = out["lse"].cpu().numpy()
+    lse_from_t = vo.unpermute(lse_t.reshape(1, heads, -1)[..., None], T, H, W)[..., 0]
+    lse_from_t = lse_from_t.transpose(0, 2, 1)
+    assert np.array_equal(lse.cpu().numpy(), lse_from_t), "raster LSE differs"
+    ref, _ = vo.attention(q, k, v, r, s, kcount, T, H, W, w.scale)
+    assert_close(f64_of(o), ref, "O raster")
+
+
+def test_attention_raster_wan13b_full_size():
+    """The raster call at the Wan2.1-1.3B shape: bitwise the tile-major call
+    followed by the unpermute (whose sampled rows the oracle checks above)."""
+    w = wl.WORKLOADS[1]
+    kcount = w.dense_counts[0]
+    say(f"attention raster {w.name} k={kcount} (generating inputs)")
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    out = _run_all(w, q, k, v, r, s, kcount)
+    o, lse = _raster(w, q, out, 0)
+    assert np.array_equal(bits_of(o), bits_of(out["o"]))
+    assert torch.isfinite(lse).all().item()
+    del out, o, lse
+    torch.cuda.empty_cache()
+
+
 def test_attention_batch2_full():
     """Two batch entries with different inputs, radii and scores (the
     workloads draw B = 1; the batch axis stacks two draws)."""

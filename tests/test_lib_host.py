@@ -197,3 +197,28 @@ def test_token_window_call_validates_before_launch():
     wide = vsa.shape(1, 1, 64, 4, 4, 4096)
     assert call(shape=ctypes.byref(wide), wsb=vsa.attn_workspace_bytes(wide, 0)) == UNSUPPORTED
     assert vsa.lib().vsa_last_error().decode()
+
+
+def test_raster_call_validates_before_launch():
+    L = vsa.lib()
+    s = vsa.shape(1, 2, 64, 8, 16, 16)
+    sp = ctypes.byref(s)
+    good = _p(0x10000)
+    ws = vsa.attn_workspace_bytes(s, 0)
+
+    def call(shape=sp, **kw):
+        a = dict(q=good, k=good, v=good, rp=good, ci=good, scale=0.125, o=good, lse=None,
+                 chunk=0, ws=good, wsb=ws)
+        a.update(kw)
+        return L.vsa_attn_fwd_raster(shape, a["q"], a["k"], a["v"], a["rp"], a["ci"], a["scale"],
+                                     a["o"], a["lse"], a["chunk"], a["ws"], a["wsb"], None)
+    assert call(q=None) == INVALID
+    assert call(q=_p(0x10008)) == INVALID      # raster rows need 16-byte alignment
+    assert call(o=None) == INVALID
+    assert call(lse=_p(0x10002)) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(chunk=-1) == INVALID
+    assert call(wsb=ws - 1) == CAPACITY
+    s96 = vsa.shape(1, 2, 96, 8, 16, 16)
+    assert call(shape=ctypes.byref(s96)) == UNSUPPORTED
+    assert vsa.lib().vsa_last_error().decode()
