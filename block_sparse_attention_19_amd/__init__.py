@@ -439,15 +439,20 @@ def attn_fwd_token_window(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tenso
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Tuple[int, int, int],
               radii: torch.Tensor, scores: torch.Tensor, dense_count: int,
               scale: Optional[float] = None, r_max: Optional[int] = None,
-              kv_chunk: int = 0) -> torch.Tensor:
+              kv_chunk: int = 0, fused: bool = True) -> torch.Tensor:
     """Block-sparse attention of bf16 q, k, v [B, N, heads, D] (token raster
-    order over the T x H x W grid) -> o [B, N, heads, D]."""
+    order over the T x H x W grid) -> o [B, N, heads, D].  fused: the raster
+    forward call (Q gathered and O written inside it); otherwise the Q permute,
+    the tile-major forward call and the O unpermute, with the same result."""
     T, H, W = grid
     B, N, heads, D = q.shape
     s = shape(B, heads, D, T, H, W)
-    q_t = tile_permute(q, s, LAYOUT_TOKEN_MAJOR)
     k_t = tile_permute(k, s, LAYOUT_TOKEN_MAJOR)
     v_t = tile_permute(v, s, LAYOUT_FEATURE_MAJOR)
     row_ptr, col_idx, _ = build_mask(radii, scores, s, dense_count, r_max, with_routed=True)
+    if fused:
+        o, _ = attn_fwd_raster(q, k_t, v_t, row_ptr, col_idx, s, scale, kv_chunk, with_lse=False)
+        return o
+    q_t = tile_permute(q, s, LAYOUT_TOKEN_MAJOR)
     o_t, _ = attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, s, scale, kv_chunk, with_lse=False)
     return tile_unpermute(o_t, s)

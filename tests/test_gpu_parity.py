@@ -429,3 +429,21 @@ def test_attention_arbitrary_csr(D, kv_chunk):
     o = vsa.tile_unpermute(o_t, sh)
     torch.cuda.synchronize()
     _check_csr_attention(w, q, k, v, rp, ci, o, lse)
+
+
+def test_attention_composed_fused_and_unfused():
+    """vsa.attention (permutes, mask, forward) with the raster forward call and
+    with the tile-major one: the same bits, within tolerance of the oracle."""
+    w = wl.custom(9, 10, 14, 2, 64, radius_set=(1, 2), cid=416)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    kcount = 2
+    say(f"attention composed T={w.T} H={w.H} W={w.W} k={kcount}")
+    args = (bf16_to_dev(q), bf16_to_dev(k), bf16_to_dev(v), (w.T, w.H, w.W),
+            torch.from_numpy(r).to(dev()), torch.from_numpy(s).to(dev()), kcount)
+    a = vsa.attention(*args, scale=w.scale, r_max=2)
+    b = vsa.attention(*args, scale=w.scale, r_max=2, fused=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(a), bits_of(b))
+    ref, _ = vo.attention(q, k, v, r, s, kcount, w.T, w.H, w.W, w.scale)
+    assert_close(f64_of(a), ref, "O composed")
