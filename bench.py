@@ -2,7 +2,8 @@
 
 A step is the whole path over one batch of synthetic, HBM-resident input:
 tile permute of K (token-major) and V (feature-major), CSR mask build from
-per-tile radii and routing scores, and the block-sparse attention forward
+per-tile radii and routing scores (on a second stream, beside the permutes),
+and the block-sparse attention forward
 (plan, flash kernel, split combine) of vsa_attn_fwd_raster, which gathers
 each query tile's rows from the raster Q and writes every token's output row
 to the raster O (the Q permute and the O unpermute, fused).  The same path
@@ -298,21 +299,26 @@ def main():
     mbuf = vsa.mask_buffers(sh, kcount, r_max, dev)
     ws = torch.empty(vsa.attn_workspace_bytes(sh, args.kv_chunk), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    stages = ["permute_kv", "mask", "attn"]
+    stages = ["permute_kv_and_mask", "attn"]
+    # The mask build (a few small, latency-bound kernels) runs on a second
+    # stream, default priority, beside the bandwidth-bound K and V permutes.
+    side = torch.cuda.Stream(device=dev)
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
+        side.wait_stream(stream)  # the previous step's attention has read the CSR
+        with torch.cuda.stream(side):
+            rp, ci, _ = vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf)
         vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=k_t)
         vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR, out=v_t)
+        stream.wait_stream(side)
         mark(1)
-        rp, ci, _ = vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf)
-        mark(2)
         vsa.attn_fwd_raster(qd, k_t, v_t, rp, ci, sh, w.scale, args.kv_chunk, out=o,
                             workspace=ws, lse_out=lse_r)
-        mark(3)
+        mark(2)
 
     def step_unfused():
         vsa.tile_permute(qd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=q_t)
