@@ -279,7 +279,7 @@ RASTER_CASES = [  # T, H, W, heads, D, radius set, routed count, kv_chunk
 def _raster(w, q, out, kv_chunk):
     """The raster call on the caller's Q, with K/V/CSR of `out`; O starts as NaN."""
     sh = _shape(w)
-    o = torch.full((1, w.T * w.H * w.W, w.heads, w.D), float("nan"), dtype=torch.bfloat16,
+    o = torch.full((w.batch, w.T * w.H * w.W, w.heads, w.D), float("nan"), dtype=torch.bfloat16,
                    device=dev())
     qd = bf16_to_dev(q)
     o, lse = vsa.attn_fwd_raster(qd, out["k_t"], out["v_t"], out["rp"], out["ci"], sh, w.scale,
@@ -342,6 +342,10 @@ def test_attention_batch2_full():
         assert np.array_equal(out["ci"][: int(orp[-1])].cpu().numpy().astype(np.int64), oci)
         ref, _ = vo.attention(q, k, v, r, s, kcount, T, H, W, ws[0].scale)
         assert_close(f64_of(out["o"]), ref, f"O batch=2 k={kcount}")
+        # the raster call on the same batch: the same bits, every element written
+        o_r, lse_r = _raster(w2, q, out, 0)
+        assert np.array_equal(bits_of(o_r), bits_of(out["o"])), "raster O differs (batch 2)"
+        assert torch.isfinite(lse_r).all().item()
 
 
 @pytest.mark.parametrize("kv_chunk", [0, 4])
