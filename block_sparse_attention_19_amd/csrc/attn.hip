@@ -211,12 +211,13 @@ struct PlanArgs {
   Comb* comb;
 };
 
-// Rows are taken in blocks of kPlanBlock = kPlanSeg * kPlanThreads.  Wave w
-// of the block holds its rows 512w + 64j + lane (j < kPlanSeg): consecutive
-// lanes read consecutive row_ptr entries and write consecutive unit records,
-// and row order is (wave, j, lane).  Row indices fit in 32 bits (rows * 64
-// tokens is checked against INT_MAX on the host), so all index arithmetic
-// here is 32-bit.
+// Rows are taken in blocks of kPlanBlock = kPlanSeg * kPlanThreads positions
+// of the plan's order (RowOrder below).  Wave w of the block holds positions
+// 512w + 64j + lane (j < kPlanSeg): consecutive lanes write consecutive unit
+// records, and the order is (wave, j, lane); their row_ptr reads gather
+// within one (batch, head).  Row indices fit in 32 bits (rows * 64 tokens is
+// checked against INT_MAX on the host), so all index arithmetic here is
+// 32-bit.
 constexpr int kPlanSeg = 8;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanBlock = kPlanSeg * kPlanThreads;
