@@ -110,11 +110,57 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     return t.contiguous()
+
+
+def _out(t: Optional[torch.Tensor], shp: tuple, dtype: torch.dtype, device: torch.device,
+         name: str) -> Optional[torch.Tensor]:
+    """A caller-supplied output buffer, checked before any launch: the kernels
+    write it through a raw pointer, so its exact shape, dtype, device and
+    contiguity must be those the call writes (None passes through)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shp):
+        raise ValueError(f"{name} must have shape {tuple(shp)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _overlap(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """True when the byte ranges of two contiguous tensors intersect."""
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
+
+
+def _same_device(device: torch.device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace(workspace: Optional[torch.Tensor], nbytes: int, device: torch.device) -> torch.Tensor:
+    """The caller's workspace if it is a contiguous uint8 buffer of at least
+    `nbytes` on `device`, else a new one; a buffer of the wrong kind raises."""
+    if workspace is None or workspace.numel() < nbytes:
+        if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != device):
+            raise ValueError(f"workspace must be a uint8 tensor on {device}")
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    return workspace
 
 
 def tile_permute(x: torch.Tensor, s: Shape, layout: int = LAYOUT_TOKEN_MAJOR,
@@ -128,6 +174,7 @@ def tile_permute(x: torch.Tensor, s: Shape, layout: int = LAYOUT_TOKEN_MAJOR,
         shp = (s.batch, s.heads, nT, s.head_dim, 64)
     if x.shape != (s.batch, s.T * s.H * s.W, s.heads, s.head_dim):
         raise ValueError(f"x has shape {tuple(x.shape)}")
+    out = _out(out, shp, torch.bfloat16, x.device, "out")
     if out is None:
         out = torch.empty(shp, dtype=torch.bfloat16, device=x.device)
     _check(lib().vsa_tile_permute(ctypes.byref(s), _ptr(x), _ptr(out), layout, _stream(x.device)),
@@ -138,9 +185,12 @@ def tile_permute(x: torch.Tensor, s: Shape, layout: int = LAYOUT_TOKEN_MAJOR,
 def tile_unpermute(o_t: torch.Tensor, s: Shape, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 [B, heads, nT*64, D] tile-major -> [B, N, heads, D] raster."""
     o_t = _require(o_t, torch.bfloat16, "o_t")
+    if o_t.shape != (s.batch, s.heads, num_tiles(s) * 64, s.head_dim):
+        raise ValueError(f"o_t has shape {tuple(o_t.shape)}")
+    ras = (s.batch, s.T * s.H * s.W, s.heads, s.head_dim)
+    out = _out(out, ras, torch.bfloat16, o_t.device, "out")
     if out is None:
-        out = torch.empty((s.batch, s.T * s.H * s.W, s.heads, s.head_dim), dtype=torch.bfloat16,
-                          device=o_t.device)
+        out = torch.empty(ras, dtype=torch.bfloat16, device=o_t.device)
     _check(lib().vsa_tile_unpermute(ctypes.byref(s), _ptr(o_t), _ptr(out), _stream(o_t.device)),
            "vsa_tile_unpermute")
     return out
@@ -177,12 +227,22 @@ def build_mask(radii: torch.Tensor, scores: torch.Tensor, s: Shape, dense_count:
         raise ValueError("radii / scores must be [B, heads, nT]")
     r_max = 255 if r_max is None else int(r_max)
     dev = radii.device
+    _same_device(dev, scores=scores)
     if out is None:
         row_ptr, col_idx, routed = mask_buffers(s, dense_count, r_max, dev)
         if not with_routed:
             routed = None
     else:
         row_ptr, col_idx, routed = out
+        rows = s.batch * s.heads * nT
+        row_ptr = _out(row_ptr, (rows + 1,), torch.int32, dev, "row_ptr")
+        if row_ptr is None:
+            raise ValueError("out must hold a row_ptr buffer")
+        if (not isinstance(col_idx, torch.Tensor) or col_idx.dim() != 1 or
+                col_idx.dtype != torch.int32 or col_idx.device != dev or
+                not col_idx.is_contiguous()):
+            raise ValueError(f"col_idx must be a contiguous 1-d int32 tensor on {dev}")
+        routed = _out(routed, (s.batch, s.heads, nT), torch.uint8, dev, "routed")
     ws_bytes = lib().vsa_mask_workspace_bytes(ctypes.byref(s))
     ws = None if routed is not None else torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     _check(lib().vsa_build_mask(ctypes.byref(s), _ptr(radii), _ptr(scores), dense_count, r_max,
@@ -204,6 +264,7 @@ def budget_to_radius(budget: torch.Tensor, s: Shape, r_max: int,
     """int32 key budgets per query token [B, heads, N] -> uint8 radii [B, heads, N]
     (the smallest tile radius whose window holds the budget, capped at r_max)."""
     budget = _token_array(budget, s, torch.int32, "budget")
+    out = _out(out, tuple(budget.shape), torch.uint8, budget.device, "out")
     if out is None:
         out = torch.empty(budget.shape, dtype=torch.uint8, device=budget.device)
     _check(lib().vsa_budget_to_radius(ctypes.byref(s), _ptr(budget), int(r_max), _ptr(out),
@@ -215,6 +276,7 @@ def tile_radius_from_tokens(token_radius: torch.Tensor, s: Shape,
                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """uint8 [B, heads, N] token radii -> uint8 [B, heads, nT] tile radii (max)."""
     token_radius = _token_array(token_radius, s, torch.uint8, "token_radius")
+    out = _out(out, (s.batch, s.heads, num_tiles(s)), torch.uint8, token_radius.device, "out")
     if out is None:
         out = torch.empty((s.batch, s.heads, num_tiles(s)), dtype=torch.uint8,
                           device=token_radius.device)
@@ -229,6 +291,7 @@ def tile_score_from_tokens(token_score: torch.Tensor, s: Shape,
     """float32 [B, heads, N] token scores -> float32 [B, heads, nT] tile scores
     (max in the IEEE-754 total order)."""
     token_score = _token_array(token_score, s, torch.float32, "token_score")
+    out = _out(out, (s.batch, s.heads, num_tiles(s)), torch.float32, token_score.device, "out")
     if out is None:
         out = torch.empty((s.batch, s.heads, num_tiles(s)), dtype=torch.float32,
                           device=token_score.device)
@@ -240,6 +303,18 @@ def tile_score_from_tokens(token_score: torch.Tensor, s: Shape,
 
 def attn_workspace_bytes(s: Shape, kv_chunk: int = 0) -> int:
     return int(lib().vsa_attn_workspace_bytes(ctypes.byref(s), kv_chunk))
+
+
+def _attn_outputs(out, lse_out, with_lse: bool, o_shape: tuple, lse_shape: tuple,
+                  device: torch.device):
+    """Output and LSE buffers of an attention call: the caller's, checked, or new."""
+    out = _out(out, o_shape, torch.bfloat16, device, "out")
+    if out is None:
+        out = torch.empty(o_shape, dtype=torch.bfloat16, device=device)
+    lse = _out(lse_out, lse_shape, torch.float32, device, "lse_out")
+    if lse is None and with_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=device)
+    return out, lse
 
 
 def attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: torch.Tensor,
@@ -263,14 +338,9 @@ def attn_fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_ptr: t
         raise ValueError("row_ptr must have B*heads*nT + 1 entries")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dev = q_t.device
-    if out is None:
-        out = torch.empty(tok, dtype=torch.bfloat16, device=dev)
-    lse = lse_out
-    if lse is None and with_lse:
-        lse = torch.empty(tok[:3], dtype=torch.float32, device=dev)
-    ws_bytes = attn_workspace_bytes(s, kv_chunk)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _same_device(dev, k_t=k_t, v_t=v_t, row_ptr=row_ptr, col_idx=col_idx)
+    out, lse = _attn_outputs(out, lse_out, with_lse, tok, tok[:3], dev)
+    workspace = _workspace(workspace, attn_workspace_bytes(s, kv_chunk), dev)
     _check(lib().vsa_attn_fwd(ctypes.byref(s), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(row_ptr),
                               _ptr(col_idx), scale, _ptr(out), _ptr(lse), kv_chunk,
                               _ptr(workspace), workspace.numel(), _stream(dev)),
@@ -303,16 +373,11 @@ def attn_fwd_raster(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_p
         raise ValueError("row_ptr must have B*heads*nT + 1 entries")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dev = q.device
-    if out is None:
-        out = torch.empty(ras, dtype=torch.bfloat16, device=dev)
-    elif out.shape != ras or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 [B, N, heads, D] tensor")
-    lse = lse_out
-    if lse is None and with_lse:
-        lse = torch.empty((s.batch, s.heads, N), dtype=torch.float32, device=dev)
-    ws_bytes = attn_workspace_bytes(s, kv_chunk)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _same_device(dev, k_t=k_t, v_t=v_t, row_ptr=row_ptr, col_idx=col_idx)
+    out, lse = _attn_outputs(out, lse_out, with_lse, ras, (s.batch, s.heads, N), dev)
+    if _overlap(out, q):
+        raise ValueError("out must not overlap q")
+    workspace = _workspace(workspace, attn_workspace_bytes(s, kv_chunk), dev)
     _check(lib().vsa_attn_fwd_raster(ctypes.byref(s), _ptr(q), _ptr(k_t), _ptr(v_t),
                                      _ptr(row_ptr), _ptr(col_idx), scale, _ptr(out), _ptr(lse),
                                      kv_chunk, _ptr(workspace), workspace.numel(), _stream(dev)),
@@ -330,12 +395,12 @@ def quantize_mxfp4(x_t: torch.Tensor, s: Shape, codes: Optional[torch.Tensor] = 
     if x_t.shape != tok:
         raise ValueError("x_t shape does not match the shape")
     dev = x_t.device
+    codes = _out(codes, tok[:3] + (D // 2,), torch.uint8, dev, "codes")
+    scales = _out(scales, tok[:3] + (D // 32,), torch.uint8, dev, "scales")
     if codes is None:
         codes = torch.empty(tok[:3] + (D // 2,), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty(tok[:3] + (D // 32,), dtype=torch.uint8, device=dev)
-    if codes.numel() < x_t.numel() // 2 or scales.numel() < x_t.numel() // 32:
-        raise ValueError("codes / scales too small")
     _check(lib().vsa_quantize_mxfp4(ctypes.byref(s), _ptr(x_t), _ptr(codes), _ptr(scales),
                                     _stream(dev)), "vsa_quantize_mxfp4")
     return codes, scales
@@ -350,8 +415,9 @@ def attn_fwd_tiered(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
                     lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """attn_fwd with a tier byte per CSR entry (non-zero = skim: the pair's
     scores from the MXFP4 q4 / k4, each a (codes, scales) pair from
-    quantize_mxfp4).  `tier` must hold at least row_ptr[-1] bytes (not checked
-    here: that count lives on the device)."""
+    quantize_mxfp4).  `tier` must hold at least row_ptr[-1] bytes, as col_idx
+    must hold row_ptr[-1] entries: that count lives on the device, so it is
+    not checked here (reading it would synchronise the stream)."""
     q_t = _require(q_t, torch.bfloat16, "q_t")
     k_t = _require(k_t, torch.bfloat16, "k_t")
     v_t = _require(v_t, torch.bfloat16, "v_t")
@@ -368,18 +434,14 @@ def attn_fwd_tiered(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
     for c, sc in ((q4c, q4s), (k4c, k4s)):
         if c.numel() != q_t.numel() // 2 or sc.numel() != q_t.numel() // 32:
             raise ValueError("MXFP4 codes / scales do not match the shape")
+    _same_device(q_t.device, q4=q4c, q4_scales=q4s, k4=k4c, k4_scales=k4s, tier=tier)
     if row_ptr.numel() != s.batch * s.heads * nT + 1:
         raise ValueError("row_ptr must have B*heads*nT + 1 entries")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dev = q_t.device
-    if out is None:
-        out = torch.empty(tok, dtype=torch.bfloat16, device=dev)
-    lse = lse_out
-    if lse is None and with_lse:
-        lse = torch.empty(tok[:3], dtype=torch.float32, device=dev)
-    ws_bytes = attn_workspace_bytes(s, kv_chunk)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _same_device(dev, k_t=k_t, v_t=v_t, row_ptr=row_ptr, col_idx=col_idx)
+    out, lse = _attn_outputs(out, lse_out, with_lse, tok, tok[:3], dev)
+    workspace = _workspace(workspace, attn_workspace_bytes(s, kv_chunk), dev)
     _check(lib().vsa_attn_fwd_tiered(ctypes.byref(s), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(q4c),
                                      _ptr(q4s), _ptr(k4c), _ptr(k4s), _ptr(row_ptr),
                                      _ptr(col_idx), _ptr(tier), scale, _ptr(out), _ptr(lse),
@@ -417,16 +479,12 @@ def attn_fwd_token_window(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tenso
     if routed.numel() != s.batch * s.heads * nT:
         raise ValueError("routed must be [B, heads, nT]")
     token_radius = _token_array(token_radius, s, torch.uint8, "token_radius")
+    _same_device(q_t.device, routed=routed, token_radius=token_radius)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dev = q_t.device
-    if out is None:
-        out = torch.empty(tok, dtype=torch.bfloat16, device=dev)
-    lse = lse_out
-    if lse is None and with_lse:
-        lse = torch.empty(tok[:3], dtype=torch.float32, device=dev)
-    ws_bytes = attn_workspace_bytes(s, kv_chunk)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _same_device(dev, k_t=k_t, v_t=v_t, row_ptr=row_ptr, col_idx=col_idx)
+    out, lse = _attn_outputs(out, lse_out, with_lse, tok, tok[:3], dev)
+    workspace = _workspace(workspace, attn_workspace_bytes(s, kv_chunk), dev)
     _check(lib().vsa_attn_fwd_token_window(ctypes.byref(s), _ptr(q_t), _ptr(k_t), _ptr(v_t),
                                            _ptr(row_ptr), _ptr(col_idx), _ptr(routed),
                                            _ptr(token_radius), int(r_max), scale, _ptr(out),

@@ -69,9 +69,7 @@ vsa_status check_shape(const vsa_shape* s) {
     set_error("batch * heads must be <= 65535");
     return VSA_ERR_INVALID_ARG;
   }
-  const Grid g = make_grid(*s);
   const int64_t nT = (int64_t)((s->T + 3) / 4) * ((s->H + 3) / 4) * ((s->W + 3) / 4);
-  (void)g;
   const int64_t rows = (int64_t)s->batch * s->heads * nT;
   // rows and padded token rows are int32 in the CSR and the unit list.
   if (nT * kTileTokens > INT_MAX || rows * kTileTokens > INT_MAX) {

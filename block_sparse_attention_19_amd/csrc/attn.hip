@@ -69,7 +69,8 @@ struct Unit {
   int32_t kb, ke;  // key range [kb, ke): offsets into row[0]'s column list
   int32_t slot;    // first partial slot, or -1: write the final output
   int32_t mode;    // 0 = G (two query tiles share the keys), 1 = S (one tile, keys split)
-  int32_t pad[2];
+  int32_t complete;  // 1: the row holds nT entries, so its keys are 0..nT-1 (G units always)
+  int32_t pad;
 };
 static_assert(sizeof(Unit) == 32, "unit layout");
 
@@ -191,6 +192,7 @@ AttnLayout attn_layout(const vsa_shape& s, int kv_chunk) {
   L.off_pml = take((size_t)L.max_slots * kTileTokens * 2 * 4);
   L.off_ext = take(4 * (size_t)g.nT);
   L.off_coord = take(4 * (size_t)g.nT);
+  L.off_iota = take(4 * (size_t)g.nT);
   L.total = o;
   return L;
 }
@@ -206,7 +208,7 @@ struct PlanArgs {
   int blk_h, blk_w;  // spatial block of the row order (see RowOrder)
   int64_t max_units, max_slots;
   Header* hdr;
-  int *cbase, *gbase, *grows, *ext, *coord;
+  int *cbase, *gbase, *grows, *ext, *coord, *iota;
   Unit* units;
   Comb* comb;
 };
@@ -409,6 +411,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   for (int tau = t; tau < nT; tau += kPlanThreads) {
     p.ext[tau] = pack_extent(tau, p.nh, p.nw, p.T, p.H, p.W);
     p.coord[tau] = pack_coord(tau, p.nh, p.nw);
+    p.iota[tau] = tau;
     if (table) s_order[ord.pos(tau)] = tau;
   }
   if (t == 0) s_front = 0;
@@ -582,7 +585,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
         u.ke = u.kb + chunk_len(len[j], n, c);
         u.slot = (n > 1) ? slot0 + c : -1;
         u.mode = 1;
-        u.pad[0] = u.pad[1] = 0;
+        u.complete = (len[j] == nT) ? 1 : 0;
+        u.pad = 0;
         const int at = is_front(u.ke - u.kb) ? atomicAdd(&s_front, 1) : rest_base + pos_rest++;
         if ((unsigned)at < (unsigned)n_units) p.units[at] = u;
       }
@@ -617,7 +621,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     u.ke = min(nT, u.kb + chunk_g);
     u.slot = (sg > 1) ? 2 * i : -1;
     u.mode = 0;
-    u.pad[0] = u.pad[1] = 0;
+    u.complete = 1;
+    u.pad = 0;
     p.units[nFront + i] = u;
   }
   if (sg > 1) {
@@ -688,6 +693,7 @@ struct AttnArgs {
   float* lse;          // [BH][nT*64], or raster [B][Hh][N]; or null
   int raster, heads;   // raster: q, o and lse in the caller's layout (tok_at)
   const int* ext;      // packed extent per key tile
+  const int* iota;     // 0 .. nT-1: the key list of a complete row
   const Header* hdr;
   Header* hdr_mut;
   const Unit* units;
@@ -1342,7 +1348,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     st.m = -INFINITY;
     st.l = 0.f;
 
-    const int* cols = args.col_idx + uni(args.row_ptr[u.row[0]]) + u.kb;
+    // A row of nT entries lists every key tile once (its columns ascend
+    // strictly within [0, nT)), so its keys are read from the plan's 0..nT-1
+    // table: both rows of a G unit walk the same keys whatever either list holds.
+    u.complete = uni(u.complete);
+    const int* cols = (g_mode || u.complete) ? args.iota + u.kb
+                                             : args.col_idx + uni(args.row_ptr[u.row[0]]) + u.kb;
     const int nkeys = u.ke - u.kb;
     const char* kbase = reinterpret_cast<const char*>(args.k) + bh * (int64_t)nT * TC * 16;
     const char* vbase = reinterpret_cast<const char*>(args.v) + bh * (int64_t)nT * TC * 16;
@@ -1513,6 +1524,7 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   pa.grows = reinterpret_cast<int*>(w + L.off_grows);
   pa.ext = reinterpret_cast<int*>(w + L.off_ext);
   pa.coord = reinterpret_cast<int*>(w + L.off_coord);
+  pa.iota = reinterpret_cast<int*>(w + L.off_iota);
   pa.nh = g.nh;
   pa.nw = g.nw;
   pa.T = s.T;
@@ -1538,6 +1550,7 @@ hipError_t launch_attn(const vsa_shape& s, const void* q, const void* k, const v
   aa.o = static_cast<uint16_t*>(o);
   aa.lse = lse;
   aa.ext = pa.ext;
+  aa.iota = pa.iota;
   aa.coord = pa.coord;
   aa.tok_r = tokw ? tokw->token_radius : nullptr;
   aa.routed = tokw ? tokw->routed : nullptr;

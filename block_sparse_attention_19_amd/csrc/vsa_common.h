@@ -47,7 +47,7 @@ __device__ __forceinline__ uint64_t tile_valid_mask(int tau, int nh, int nw, int
 struct AttnLayout {
   int64_t rows, bh, max_units, max_slots;
   size_t off_cbase, off_gbase, off_grows, off_units, off_comb, off_po, off_pml, off_ext,
-      off_coord, total;
+      off_coord, off_iota, total;
 };
 
 // Launchers (one per source file); each returns the launch status.

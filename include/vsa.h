@@ -95,9 +95,14 @@ vsa_status vsa_tile_permute(const vsa_shape* s, const void* x, void* x_tiled,
                             int32_t layout, void* stream);
 
 /* vsa_tile_unpermute: inverse of the token-major permute for the attention
- * output; padded rows of o_tiled are never read.
+ * output, returning each real token's row to raster order (TRA, pipeline
+ * step 3: attention runs in the tile-major layout; the outputs of padding
+ * slots, which hold no token, are dropped).  Padded rows of o_tiled are never
+ * read.
  *   o_tiled  bf16 [B][heads][nT*64][D]
- *   o        bf16 [B][N][heads][D]
+ *   o        bf16 [B][N][heads][D], every element written.
+ * Errors: INVALID_ARG for a bad shape or a NULL / misaligned pointer;
+ * OVERFLOW as vsa_tile_permute.
  */
 vsa_status vsa_tile_unpermute(const vsa_shape* s, const void* o_tiled, void* o,
                               void* stream);
@@ -184,17 +189,26 @@ vsa_status vsa_tile_score_from_tokens(const vsa_shape* s, const float* token_sco
  */
 size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk);
 
-/* vsa_attn_fwd: block-sparse attention forward over the tile-major layout.
- * Walks only the key tiles listed in the CSR, with bf16 MFMA products, fp32
- * online softmax and accumulation; long rows are split across workgroups
- * and merged exactly by log-sum-exp (the split never changes which keys a
- * query sees, only the fp32 summation order).
+/* vsa_attn_fwd: block-sparse attention forward over the tile-major layout
+ * (TRA, pipeline step 3: attention executed on the retained blocks of the
+ * block-sparse mask only; Triage, "A tile-by-tile choice": skipped tiles cost
+ * nothing).  The result is masked softmax attention over the listed key
+ * tiles.  Walks only the key tiles listed in the CSR, with bf16 MFMA
+ * products, fp32 online softmax and accumulation; long rows are split across
+ * workgroups and merged exactly by log-sum-exp (the split never changes
+ * which keys a query sees, only the fp32 summation order).
  *   q_t      bf16 [B][heads][nT*64][D]  (VSA_LAYOUT_TOKEN_MAJOR)
  *   k_t      bf16 [B][heads][nT*64][D]  (VSA_LAYOUT_TOKEN_MAJOR)
  *   v_t      bf16 [B][heads][nT][D][64] (VSA_LAYOUT_FEATURE_MAJOR)
- *   row_ptr, col_idx: a CSR as vsa_build_mask writes it (rows (b, h, a);
- *            columns ascending, in [0, nT)); any such CSR is accepted.
- *            A row with no column yields zeros and LSE = -inf.
+ *   row_ptr, col_idx: a CSR over rows (b, h, a) (row_ptr non-decreasing,
+ *            row_ptr[0] = 0).  Each row's columns must lie in [0, nT) and
+ *            ascend strictly (no repeats), as vsa_build_mask writes them;
+ *            columns outside [0, nT) are not checked and read outside k_t
+ *            and v_t.  Any other CSR of that kind is accepted.  A row of
+ *            exactly nT entries is therefore every key tile, and the call
+ *            attends key tiles 0..nT-1 for it without reading its columns;
+ *            a shorter row with a repeated column attends that tile once per
+ *            occurrence.  A row with no column yields zeros and LSE = -inf.
  *   scale    softmax scale (1/sqrt(D) for standard attention), finite, > 0.
  *   o_t      bf16 [B][heads][nT*64][D]: outputs; rows of padding query slots
  *            hold unspecified values.
@@ -205,7 +219,10 @@ size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk);
  *   ws, ws_bytes device workspace of at least vsa_attn_workspace_bytes(s,
  *            kv_chunk); its contents need no initialisation.
  * Padding keys (slots outside the grid) are excluded from every softmax by
- * position, whatever values they hold.
+ * position: their K values never matter, and their V values are multiplied
+ * by a probability of exactly 0, so they must be finite (the permute writes
+ * +0.0 there); a NaN or infinity in a padded V slot makes the outputs of the
+ * query tiles that list that key tile NaN.
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim not 64/128), CAPACITY (ws),
  * OVERFLOW.
  */

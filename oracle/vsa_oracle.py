@@ -358,10 +358,6 @@ def partial_attention(q, k, v, scale: float):
 
 # ------------------------------------------------------------- derived counts
 
-def retained_pairs(row_ptr: np.ndarray) -> int:
-    return int(row_ptr[-1])
-
-
 def window_count_closed_form(r: int) -> int:
     """Key tiles kept by an interior (unclipped) query tile of radius r:
     sum over dt in [-r, r] of the (2(r-|dt|)+1)^2 spatial square."""

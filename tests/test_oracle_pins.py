@@ -165,6 +165,54 @@ def test_fitted_dense_count():
     assert fit_dense_count.fit(r, s, w.T, w.H, w.W) == wl.HUNYUAN_FITTED_DENSE_COUNT
 
 
+@pytest.mark.parametrize("T,H,W,rset", [(9, 10, 11, (1, 2, 3, 4)), (13, 9, 17, (0, 1, 2, 3))])
+def test_density_by_count_vs_block_mask(T, H, W, rset):
+    """The incremental density of fit_dense_count (each further routed tile adds
+    its missing key tiles) equals the density of the mask built from scratch,
+    for every routed count."""
+    from oracle import fit_dense_count
+    w = wl.custom(T, H, W, 3, 64, radius_set=rset, cid=310 + T)
+    r, s = wl.radii_scores(w)
+    d = fit_dense_count.density_by_count(r, s, T, H, W)
+    n = vo.num_tiles(T, H, W)
+    assert d.shape == (n + 1,)
+    for k in range(n + 1):
+        keep, _ = vo.block_mask(r, s, k, T, H, W)
+        assert d[k] == pytest.approx(keep.mean(), abs=1e-13), k
+    assert np.all(np.diff(d) >= 0)
+
+
+def test_density_by_count_vs_brute():
+    """The same against the pure-Python CSR on a tiny ragged grid, every k."""
+    from oracle import fit_dense_count
+    T, H, W = 5, 9, 6
+    w = wl.custom(T, H, W, 2, 64, radius_set=(0, 1, 2), cid=320)
+    r, s = wl.radii_scores(w)
+    d = fit_dense_count.density_by_count(r, s, T, H, W)
+    n = vo.num_tiles(T, H, W)
+    for k in range(n + 1):
+        rp, _ = brute.csr(r[0].tolist(), s[0].tolist(), k, T, H, W)
+        assert d[k] == pytest.approx(rp[-1] / (2 * n * n), abs=1e-13), k
+
+
+def test_fitted_dense_count_direct():
+    """HunyuanVideo-shaped call: the retained density of the masks built at
+    k = 143, 144, 145 routed tiles (straight from the keep rule), and 144 the
+    count closest to 10% (density grows with k, so the closest count is one of
+    the two around the crossing)."""
+    w = wl.WORKLOADS[4]
+    r, s = wl.radii_scores(w)
+    dens = {}
+    for k in (143, 144, 145):
+        keep, _ = vo.block_mask(r, s, k, w.T, w.H, w.W)
+        dens[k] = keep.mean()
+    assert round(dens[143], 5) == 0.09968
+    assert round(dens[144], 5) == 0.10012
+    assert round(dens[145], 5) == 0.10057
+    assert dens[143] < 0.10 <= dens[144]
+    assert min(dens, key=lambda k: abs(dens[k] - 0.10)) == wl.HUNYUAN_FITTED_DENSE_COUNT
+
+
 # ---------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,H,W", GRIDS + [(8, 16, 16), (21, 30, 52)])
