@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         "vsa_attn_workspace_bytes": (SZ, [SP, I32]),
         "vsa_attn_fwd": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, I32, P, SZ, P]),
         "vsa_attn_fwd_raster": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, I32, P, SZ, P]),
+        "vsa_attn_noalloc_max_workspace": (SZ, []),
+        "vsa_attn_fwd_raster_noalloc": (ctypes.c_int, [SP, P, P, P, P, P, ctypes.c_float, P, P, P]),
         "vsa_quantize_mxfp4": (ctypes.c_int, [SP, P, P, P, P]),
         "vsa_attn_fwd_tiered": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
                                                P, P, I32, P, SZ, P]),
@@ -382,6 +384,48 @@ def attn_fwd_raster(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, row_p
                                      _ptr(row_ptr), _ptr(col_idx), scale, _ptr(out), _ptr(lse),
                                      kv_chunk, _ptr(workspace), workspace.numel(), _stream(dev)),
            "vsa_attn_fwd_raster")
+    return out, lse
+
+
+def attn_noalloc_max_workspace() -> int:
+    """Bytes of the library's fixed workspace used by attn_fwd_raster_noalloc."""
+    return int(lib().vsa_attn_noalloc_max_workspace())
+
+
+def attn_fwd_raster_noalloc(q: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
+                            row_ptr: torch.Tensor, col_idx: torch.Tensor, s: Shape,
+                            scale: Optional[float] = None, with_lse: bool = True,
+                            out: Optional[torch.Tensor] = None,
+                            lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """attn_fwd_raster (kv_chunk 0) on the library's fixed device workspace:
+    the C call allocates nothing (outputs passed here are used as given; None
+    allocates them on the PyTorch side).  Calls in flight at once on one GPU
+    share that workspace and must be serialised."""
+    q = _require(q, torch.bfloat16, "q")
+    k_t = _require(k_t, torch.bfloat16, "k_t")
+    v_t = _require(v_t, torch.bfloat16, "v_t")
+    row_ptr = _require(row_ptr, torch.int32, "row_ptr")
+    col_idx = _require(col_idx, torch.int32, "col_idx")
+    nT = num_tiles(s)
+    D = s.head_dim
+    N = s.T * s.H * s.W
+    ras = (s.batch, N, s.heads, D)
+    if q.shape != ras:
+        raise ValueError("q must be [B, N, heads, D]")
+    if k_t.shape != (s.batch, s.heads, nT * 64, D) or v_t.shape != (s.batch, s.heads, nT, D, 64):
+        raise ValueError("k_t / v_t shapes do not match the shape")
+    if row_ptr.numel() != s.batch * s.heads * nT + 1:
+        raise ValueError("row_ptr must have B*heads*nT + 1 entries")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q.device
+    _same_device(dev, k_t=k_t, v_t=v_t, row_ptr=row_ptr, col_idx=col_idx)
+    out, lse = _attn_outputs(out, lse_out, with_lse, ras, (s.batch, s.heads, N), dev)
+    if _overlap(out, q):
+        raise ValueError("out must not overlap q")
+    _check(lib().vsa_attn_fwd_raster_noalloc(ctypes.byref(s), _ptr(q), _ptr(k_t), _ptr(v_t),
+                                             _ptr(row_ptr), _ptr(col_idx), scale, _ptr(out),
+                                             _ptr(lse), _stream(dev)),
+           "vsa_attn_fwd_raster_noalloc")
     return out, lse
 
 

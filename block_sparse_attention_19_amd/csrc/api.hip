@@ -52,6 +52,38 @@ vsa_status device_cus(int* cus) {
   return VSA_OK;
 }
 
+// Device-resident workspace of the allocation-free forward call: one copy per
+// GPU (each device that loads the library holds its own until the process
+// ends).  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = size_t(48) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch_dev[kMaxDevices] = {nullptr};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current).
+vsa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("hipGetDevice failed: %s", hipGetErrorString(e));
+    return VSA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      set_error("hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return VSA_ERR_HIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return VSA_OK;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 vsa_status check_shape(const vsa_shape* s) {
@@ -255,12 +287,11 @@ size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk) {
   return attn_layout(*s, kv_chunk).total;
 }
 
-// Argument checks shared by the tile-major and the raster forward calls.
-static vsa_status check_attn_args(const vsa_shape* s, const void* q, const char* q_name,
-                                  const void* k_t, const void* v_t, const int32_t* row_ptr,
-                                  const int32_t* col_idx, float scale, const void* o,
-                                  const char* o_name, const float* lse, const char* lse_name,
-                                  int32_t kv_chunk, const void* ws, size_t ws_bytes) {
+// Checks of the inputs, outputs and scale shared by every forward call.
+static vsa_status check_attn_io(const vsa_shape* s, const void* q, const char* q_name,
+                                const void* k_t, const void* v_t, const int32_t* row_ptr,
+                                const int32_t* col_idx, float scale, const void* o,
+                                const char* o_name, const float* lse, const char* lse_name) {
   VSA_TRY(check_shape(s));
   VSA_TRY(check_ptr(q, 16, q_name));
   VSA_TRY(check_ptr(k_t, 16, "k_t"));
@@ -269,11 +300,22 @@ static vsa_status check_attn_args(const vsa_shape* s, const void* q, const char*
   VSA_TRY(check_ptr(col_idx, 4, "col_idx"));
   VSA_TRY(check_ptr(o, 16, o_name));
   if (lse) VSA_TRY(check_ptr(lse, 4, lse_name));
-  VSA_TRY(check_ptr(ws, 256, "ws"));
   if (!(scale > 0.f) || scale > 3.0e38f) {
     set_error("scale must be finite and > 0");
     return VSA_ERR_INVALID_ARG;
   }
+  return VSA_OK;
+}
+
+// Argument checks shared by the tile-major and the raster forward calls.
+static vsa_status check_attn_args(const vsa_shape* s, const void* q, const char* q_name,
+                                  const void* k_t, const void* v_t, const int32_t* row_ptr,
+                                  const int32_t* col_idx, float scale, const void* o,
+                                  const char* o_name, const float* lse, const char* lse_name,
+                                  int32_t kv_chunk, const void* ws, size_t ws_bytes) {
+  VSA_TRY(check_attn_io(s, q, q_name, k_t, v_t, row_ptr, col_idx, scale, o, o_name, lse,
+                        lse_name));
+  VSA_TRY(check_ptr(ws, 256, "ws"));
   if (kv_chunk < 0) {
     set_error("kv_chunk must be >= 0");
     return VSA_ERR_INVALID_ARG;
@@ -308,6 +350,29 @@ vsa_status vsa_attn_fwd_raster(const vsa_shape* s, const void* q, const void* k_
   VSA_TRY(device_cus(&cus));
   return hip_status(launch_attn(*s, q, k_t, v_t, row_ptr, col_idx, scale, o, lse, kv_chunk, ws,
                                 cus, static_cast<hipStream_t>(stream), nullptr, nullptr, true),
+                    "attention launch");
+}
+
+size_t vsa_attn_noalloc_max_workspace(void) { return kScratchBytes; }
+
+vsa_status vsa_attn_fwd_raster_noalloc(const vsa_shape* s, const void* q, const void* k_t,
+                                       const void* v_t, const int32_t* row_ptr,
+                                       const int32_t* col_idx, float scale, void* o, float* lse,
+                                       void* stream) {
+  VSA_TRY(check_attn_io(s, q, "q", k_t, v_t, row_ptr, col_idx, scale, o, "o", lse, "lse"));
+  const size_t need = attn_layout(*s, 0).total;
+  if (need > kScratchBytes) {
+    set_error("shape needs %zu bytes of workspace; the allocation-free call holds %zu "
+              "(use vsa_attn_fwd_raster with a caller workspace)",
+              need, kScratchBytes);
+    return VSA_ERR_CAPACITY;
+  }
+  void* ws = nullptr;
+  VSA_TRY(scratch_address(&ws));
+  int cus = 0;
+  VSA_TRY(device_cus(&cus));
+  return hip_status(launch_attn(*s, q, k_t, v_t, row_ptr, col_idx, scale, o, lse, 0, ws, cus,
+                                static_cast<hipStream_t>(stream), nullptr, nullptr, true),
                     "attention launch");
 }
 

@@ -253,6 +253,34 @@ vsa_status vsa_attn_fwd_raster(const vsa_shape* s, const void* q, const void* k_
                                float scale, void* o, float* lse, int32_t kv_chunk, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- allocation-free call
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the raster
+ * forward call with its workspace taken from a fixed device array inside the
+ * library instead of a caller buffer.  The library allocates nothing on this
+ * path (no hipMalloc, no allocating library routine); the array is part of
+ * the loaded code object, one copy per GPU, held until the process ends.
+ *
+ * vsa_attn_noalloc_max_workspace: the array's size in bytes (48 MiB); a
+ * shape fits when vsa_attn_workspace_bytes(s, 0) is at most this.
+ *
+ * vsa_attn_fwd_raster_noalloc: vsa_attn_fwd_raster with kv_chunk = 0 and
+ * that array as its workspace; the same kernels, so O and LSE are bitwise
+ * those of vsa_attn_fwd_raster.  Every call on a GPU uses that GPU's one
+ * array, and nothing in it needs to start at zero (each call's plan writes
+ * what the call reads), but two calls in flight at once on the same GPU (on
+ * different streams, or from different threads) race on it: serialise them.
+ *   q, k_t, v_t, row_ptr, col_idx, scale, o, lse: as vsa_attn_fwd_raster.
+ * Errors: as vsa_attn_fwd_raster; CAPACITY when the shape needs more than
+ * vsa_attn_noalloc_max_workspace() bytes (nothing is enqueued then).
+ */
+size_t vsa_attn_noalloc_max_workspace(void);
+
+vsa_status vsa_attn_fwd_raster_noalloc(const vsa_shape* s, const void* q, const void* k_t,
+                                       const void* v_t, const int32_t* row_ptr,
+                                       const int32_t* col_idx, float scale, void* o,
+                                       float* lse, void* stream);
+
 /* ----------------------------------------------------- low-precision tier
  * "Triage: Skip, Skim, or Refine Attention Tiles in Video Diffusion
  * Transformers" (plain-words summary; "Route by estimated error"): every

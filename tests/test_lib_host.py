@@ -222,3 +222,32 @@ def test_raster_call_validates_before_launch():
     s96 = vsa.shape(1, 2, 96, 8, 16, 16)
     assert call(shape=ctypes.byref(s96)) == UNSUPPORTED
     assert vsa.lib().vsa_last_error().decode()
+
+
+def test_noalloc_call_validates_before_launch():
+    """The allocation-free forward call: its fixed workspace size, argument
+    checks, and a shape that needs more workspace than it holds is refused with
+    CAPACITY (all before any HIP call)."""
+    L = vsa.lib()
+    cap = vsa.attn_noalloc_max_workspace()
+    assert cap == 48 << 20
+    good = _p(0x10000)
+    s = vsa.shape(1, 12, 128, 21, 30, 52)
+    sp = ctypes.byref(s)
+    assert vsa.attn_workspace_bytes(s, 0) <= cap
+    fn = L.vsa_attn_fwd_raster_noalloc
+    assert fn(sp, None, good, good, good, good, 0.125, good, None, None) == INVALID
+    assert fn(sp, good, good, good, good, good, 0.0, good, None, None) == INVALID
+    assert fn(sp, good, good, good, good, good, 0.125, _p(0x10008), None, None) == INVALID
+    assert fn(sp, good, good, good, good, good, 0.125, good, _p(0x10002), None) == INVALID
+    assert fn(None, good, good, good, good, good, 0.125, good, None, None) == INVALID
+    # 32 batch entries of the HunyuanVideo grid (1.66M tile rows) exceed it
+    big = vsa.shape(32, 24, 128, 33, 45, 80)
+    assert vsa.attn_workspace_bytes(big, 0) > cap
+    assert fn(ctypes.byref(big), good, good, good, good, good, 0.125, good, None, None) == CAPACITY
+    assert "allocation-free" in L.vsa_last_error().decode()
+    # every workload of the benchmark fits
+    import workloads as wl
+    for c in range(5):
+        w = wl.WORKLOADS[c]
+        assert vsa.attn_workspace_bytes(vsa.shape(w.batch, w.heads, w.D, w.T, w.H, w.W), 0) <= cap
