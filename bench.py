@@ -21,7 +21,16 @@ tile radius, tile score) and ``skim_tier`` the MXFP4 encoding and the tiered
 attention call (half / all kept pairs skimmed) at the workload's size, both
 outside the step.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 30] [--workload 1]
+Beside the headline, ``configs`` measures every workload and routing point
+(Wan2.1-1.3B, the Wan2.2-5B sweep of 20/0/10/40/100% routed, Wan2.1-14B,
+HunyuanVideo at the fitted count and all routed): the attention call warm
+(median, p10, p90, mean over per-launch events) and cold (1 GiB rewritten
+before each launch, so neither the L2 nor the Infinity Cache holds K and V),
+the K and V permutes, the mask build and the O unpermute in GB/s of
+algorithmic bytes, the step, and the speedup over the dense-mask run of the
+same shape.
+
+    python bench.py [--gpus 1] [--steps 30] [--warmup 30] [--workload 1] [--no-configs]
 """
 from __future__ import annotations
 
@@ -55,7 +64,41 @@ def parse():
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload leg (configs)")
+    ap.add_argument("--no-side-legs", action="store_true",
+                    help="skip the token-level, per-token-window and skim-tier legs")
+    ap.add_argument("--cold-reps", type=int, default=8,
+                    help="launches timed after a cache flush, per measurement")
     return ap.parse_args()
+
+
+FLUSH_BYTES = 1 << 30   # rewritten before a cold launch: 4x the 256 MB Infinity Cache
+
+
+def _pcts(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4),
+            "n": int(a.size)}
+
+
+def time_launches(fn, stream, reps, flush=None):
+    """Per-launch durations (ms) of fn() on `stream`, each bracketed by its own
+    pair of HIP events; with `flush`, a buffer of FLUSH_BYTES is rewritten
+    (read and written) before every launch, outside the bracket."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush.add_(1)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
 def attn_source_hash() -> str:
@@ -81,11 +124,14 @@ def cpu_baseline(w, q, k, v, r, s, kcount, budget_s):
     budget is spent; rated in retained-tile TFLOP/s like the GPU."""
     import numpy as np
     from oracle import vsa_oracle as vo
+    # the host cores this process may run on; numpy's BLAS (the oracle's
+    # matrix products) is given exactly that many threads
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        limiter = None
     rng = np.random.default_rng(1234)
     tt = vo.token_tile(w.T, w.H, w.W)
     done_tiles, pairs, t0 = 0, 0, time.perf_counter()
@@ -99,6 +145,8 @@ def cpu_baseline(w, q, k, v, r, s, kcount, budget_s):
             done_tiles += 1
             pairs += int(keep[a].sum())
     el = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     flops = pairs * 4.0 * 64 * 64 * w.D
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done_tiles} query tiles ({pairs} retained tile pairs) of {w.name}, "
@@ -212,6 +260,113 @@ def token_windows(w, sh, dev, stream, reps, q_t, k_t, v_t, ws, o_t, kv_chunk, kc
                                   "TFLOP/s": round(flops / (ms_w * 1e-3) / 1e12, 2)},
             "attn_block_mask_same_csr": {"ms": round(ms_b, 4),
                                          "TFLOP/s": round(flops / (ms_b * 1e-3) / 1e12, 2)}}
+
+
+# (workload, routed-count index) of the per-workload leg, in the order run
+CONFIG_POINTS = [(1, 0), (2, 0), (2, 1), (2, 2), (2, 3), (2, 4), (3, 0), (4, 0), (4, 1)]
+
+
+def configs_leg(stream, cold_reps, flush):
+    """Every workload and routing point: attention warm and cold, the K and V
+    permutes, the mask build and the O unpermute (GB/s of algorithmic bytes),
+    the step, and the dense-mask speedups.  Reps per point are scaled to the
+    call's length so the leg stays within a few tens of seconds of GPU time."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_19_amd as vsa
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    out = {}
+    by_cid = {}
+    for cid, ki in CONFIG_POINTS:
+        by_cid.setdefault(cid, []).append(ki)
+    for cid, kis in by_cid.items():
+        w = wl.WORKLOADS[cid]
+        q, k, v = wl.qkv(w)
+        r, s = wl.radii_scores(w)
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        del q, k, v
+        rd, sd = torch.from_numpy(r).to(dev), torch.from_numpy(s).to(dev)
+        sh = vsa.shape(w.batch, w.heads, w.D, w.T, w.H, w.W)
+        nT = w.n_cells
+        r_max = max(w.radius_set)
+        k_t = torch.empty((1, w.heads, nT * 64, w.D), dtype=torch.bfloat16, device=dev)
+        v_t = torch.empty((1, w.heads, nT, w.D, 64), dtype=torch.bfloat16, device=dev)
+        o = torch.empty_like(qd)
+        o_t = torch.empty_like(k_t)
+        lse = torch.empty((1, w.heads, w.tokens), dtype=torch.float32, device=dev)
+        ws = torch.empty(vsa.attn_workspace_bytes(sh, 0), dtype=torch.uint8, device=dev)
+        tok_bytes = w.tokens * w.heads * w.D * 2
+        pad_bytes = nT * 64 * w.heads * w.D * 2
+        for ki in kis:
+            kcount = w.dense_counts[ki]
+            mbuf = vsa.mask_buffers(sh, kcount, r_max, dev)
+            vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=k_t)
+            vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR, out=v_t)
+            vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf)
+            torch.cuda.synchronize()
+            rp, ci = mbuf[0], mbuf[1]
+            nnz = int(rp[-1].item())
+            flops = nnz * 4.0 * 64 * 64 * w.D
+
+            def attn():
+                vsa.attn_fwd_raster(qd, k_t, v_t, rp, ci, sh, w.scale, 0, out=o, workspace=ws,
+                                    lse_out=lse)
+
+            def step():
+                vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=k_t)
+                vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR, out=v_t)
+                vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf)
+                attn()
+
+            est = max(flops / 1.0e15 * 1e3, 0.5)           # ms at about 1 PFLOP/s
+            reps = int(min(30, max(4, 600.0 / est)))
+            for _ in range(3):
+                attn()
+            warm = time_launches(attn, stream, reps)
+            cold = time_launches(attn, stream, min(cold_reps, reps), flush=flush)
+            steps = time_launches(step, stream, max(3, reps // 2))
+            kperm = time_launches(lambda: vsa.tile_permute(kd, sh, vsa.LAYOUT_TOKEN_MAJOR, out=k_t),
+                                  stream, 10)
+            vperm = time_launches(lambda: vsa.tile_permute(vd, sh, vsa.LAYOUT_FEATURE_MAJOR, out=v_t),
+                                  stream, 10)
+            mask = time_launches(lambda: vsa.build_mask(rd, sd, sh, kcount, r_max, out=mbuf),
+                                 stream, 10)
+            unperm = time_launches(lambda: vsa.tile_unpermute(o_t, sh, out=o), stream, 10)
+            rows = w.heads * nT
+            mask_bytes = rows * (1 + 4) + 4 * (rows + 1) + 4 * nnz + rows   # radii, scores, row_ptr, col_idx, routed
+            gbs = lambda b, ms: round(b / (float(np.median(ms)) * 1e-3) / 1e9, 1)
+            wp = _pcts(warm)
+            key = f"{w.name}@k={kcount}"
+            out[key] = {
+                "workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": w.D,
+                "tiles": nT, "dense_count": kcount, "routed_fraction": round(kcount / nT, 4),
+                "retained_tile_pairs": nnz, "tile_pair_density": round(nnz / (w.heads * nT * nT), 4),
+                "attn_ms_warm": wp, "attn_ms_cold": _pcts(cold),
+                "attn_TFLOP/s": round(flops / (wp["mean"] * 1e-3) / 1e12, 2),
+                "attn_frac_of_bf16_peak": round(flops / (wp["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "attn_frac_cold": round(flops / (_pcts(cold)["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "step_ms": _pcts(steps)["median"],
+                "permute_k": {"ms": round(float(np.median(kperm)), 4), "GB/s": gbs(tok_bytes + pad_bytes, kperm)},
+                "permute_v": {"ms": round(float(np.median(vperm)), 4), "GB/s": gbs(tok_bytes + pad_bytes, vperm)},
+                "mask_build": {"ms": round(float(np.median(mask)), 4), "GB/s": gbs(mask_bytes, mask),
+                               "bytes": int(mask_bytes)},
+                "unpermute_o": {"ms": round(float(np.median(unperm)), 4), "GB/s": gbs(2 * tok_bytes, unperm)},
+            }
+            del mbuf
+        del qd, kd, vd, k_t, v_t, o, o_t, lse, ws
+        torch.cuda.empty_cache()
+    # dense-mask speedup: the same shape with every query tile routed
+    for name, sparse_k, dense_k in (("hunyuanvideo-720p-129f", wl.WORKLOADS[4].dense_counts[0],
+                                     wl.WORKLOADS[4].dense_counts[1]),
+                                    ("wan2.2-5b-720p", wl.WORKLOADS[2].dense_counts[0],
+                                     wl.WORKLOADS[2].dense_counts[4])):
+        a, b = out.get(f"{name}@k={sparse_k}"), out.get(f"{name}@k={dense_k}")
+        if a and b:
+            a["speedup_vs_dense_mask"] = round(b["attn_ms_warm"]["mean"] / a["attn_ms_warm"]["mean"], 3)
+    return out
 
 
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 MFMA (the skim tier's score products)
@@ -363,6 +518,17 @@ def main():
     u1.record(stream)
     torch.cuda.synchronize()
     ms_attn_tiled = u0.elapsed_time(u1) / args.steps
+    # per-launch attention durations of the timed steps, and the same call
+    # cold: 1 GiB rewritten before each launch (the step's K and V permutes
+    # otherwise leave K and V in the Infinity Cache for the attention call)
+    attn_launch_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    rp_, ci_ = mbuf[0], mbuf[1]
+    cold_attn = time_launches(lambda: vsa.attn_fwd_raster(qd, k_t, v_t, rp_, ci_, sh, w.scale,
+                                                          args.kv_chunk, out=o, workspace=ws,
+                                                          lse_out=lse_r),
+                              stream, args.cold_reps, flush=flush)
+    cold_step = time_launches(step, stream, args.cold_reps, flush=flush)
     nnz = int(mbuf[0][-1].item())
     flops = nnz * 4.0 * 64 * 64 * w.D
     # valid-token flops: each kept pair weighted by valid queries x valid keys
@@ -396,17 +562,29 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_figure(1.0),
+                     "traffic_basis": "bytes beyond the XCD L2s per attn_kernel launch "
+                                      "(TCC FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel); "
+                                      "the Infinity Cache may serve part of them, no counter "
+                                      "separates its hits from HBM",
                      "kernel": "vsa_attn_fwd_raster (plan + attn_kernel + combine_kernel)"},
+        "attn_ms_warm": _pcts(attn_launch_ms),
+        "attn_ms_cold": _pcts(cold_attn),
+        "attn_frac_cold": round(flops / (float(np.median(cold_attn)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_ms_cold": _pcts(cold_step),
         "breakdown_ms": {k2: round(v2, 4) for k2, v2 in per_stage.items()},
         "step_unfused_ms": round(ms_unfused, 4),
         "attn_tile_major_ms": round(ms_attn_tiled, 4),
         "attn_valid_token_tflops": round(valid_flops / (attn_ms * 1e-3) / 1e12, 2),
     }
-    line["token_level_calls"] = token_level_calls(w, sh, dev, stream, args.steps)
-    line["token_windows"] = token_windows(w, sh, dev, stream, args.steps, q_t, k_t, v_t, ws, o_t,
-                                          args.kv_chunk, kcount)
-    line["skim_tier"] = skim_tier(w, sh, dev, stream, args.steps, q_t, k_t, v_t, mbuf[0], mbuf[1],
-                                  nnz, ws, o_t, ms_attn_tiled, args.kv_chunk)
+    if not args.no_side_legs:
+        line["token_level_calls"] = token_level_calls(w, sh, dev, stream, args.steps)
+        line["token_windows"] = token_windows(w, sh, dev, stream, args.steps, q_t, k_t, v_t, ws,
+                                              o_t, args.kv_chunk, kcount)
+        line["skim_tier"] = skim_tier(w, sh, dev, stream, args.steps, q_t, k_t, v_t, mbuf[0],
+                                      mbuf[1], nnz, ws, o_t, ms_attn_tiled, args.kv_chunk)
+    del q_t, o_t, lse
+    if not args.no_configs:
+        line["configs"] = configs_leg(stream, args.cold_reps, flush)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, r, s, kcount, args.cpu_seconds)
     else:
