@@ -21,7 +21,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvsa.so")
+# The in-tree build; VSA_LIBRARY names another build of the same library (the
+# sanitizer-instrumented copy that build_lib --sanitize writes, for host tests).
+LIB_PATH = os.environ.get("VSA_LIBRARY") or os.path.join(_HERE, "libvsa.so")
 
 LAYOUT_TOKEN_MAJOR = 0
 LAYOUT_FEATURE_MAJOR = 1
