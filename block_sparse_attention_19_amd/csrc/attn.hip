@@ -40,6 +40,8 @@
 
 #include <limits.h>
 
+#include <type_traits>
+
 namespace vsa {
 namespace {
 
@@ -714,6 +716,18 @@ struct AttnArgs {
   float c2;            // scale * log2(e)
 };
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (a loop whose index
+// must be a compile-time constant, e.g. an instruction's immediate operand).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
 // Broadcast a wave-uniform value to a scalar register (the compiler cannot
 // prove uniformity of values derived from the thread index or read from LDS).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -997,6 +1011,15 @@ __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, uint32_t lane_o
                                        char* lds_block) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (VSA_LDS void*)lds_block, 16, lane_off, soff, 0, 0);
 }
+// The same with an immediate offset IMM, which the hardware adds to both the
+// source offset and the LDS address: the blocks of a run of consecutive 1 KB
+// blocks then share one LDS base (M0) and one scalar offset, so the copy loop
+// holds two scalar values per run instead of two per block.
+template <int IMM>
+__device__ __forceinline__ void dma16b_imm(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t soff,
+                                           char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (VSA_LDS void*)lds_base, 16, lane_off, soff, IMM, 0);
+}
 
 // All blocks of one K tile and one V^T tile, spread over the 4 waves of the
 // workgroup (this is wave `w`).
@@ -1009,13 +1032,15 @@ __device__ __forceinline__ void dma_tile(char* buf, const char* ktile, const cha
   constexpr int kRpb = 1024 / Cfg<D>::kRowBytes;
   (void)nw;
   const __amdgpu_buffer_rsrc_t rk = tile_rsrc(ktile, TB), rv = tile_rsrc(vtile, TB);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int blk = w * kPer + i;  // rows blk*kRpb.. (K) / blk*8.. (V); the swizzle
-                                   // phase depends on i only (w*kPer*kRpb % 16 == 0)
-    if (with_k) dma16b(rk, k_lane_off<D>(i * kRpb, lane), blk * 1024, buf + blk * 1024);
-    dma16b(rv, v_lane_off(i * 8, lane), blk * 1024, buf + TB + blk * 1024);
-  }
+  // this wave's blocks w*kPer .. w*kPer+kPer-1 (rows blk*kRpb.. of K, blk*8.. of
+  // V^T); the swizzle phase depends on i only (w*kPer*kRpb % 16 == 0)
+  static_assert(kPer <= 4, "immediate offsets reach 3 KB");
+  const int b0 = w * kPer * 1024;
+  static_for<kPer>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (with_k) dma16b_imm<i * 1024>(rk, k_lane_off<D>(i * kRpb, lane), b0, buf + b0);
+    dma16b_imm<i * 1024>(rv, v_lane_off(i * 8, lane), b0, buf + TB + b0);
+  });
 }
 
 // Per-lane byte offset, within a 1 KB block of MXFP4 K codes, of the global
@@ -1173,13 +1198,17 @@ __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const cha
   constexpr int kKBlocks = KH / 1024, kVBlocks = D * 64 / 1024;
   (void)nwv;
   const __amdgpu_buffer_rsrc_t rk = tile_rsrc(ktile, TB), rv = tile_rsrc(vtile, TB);
-#pragma unroll
-  for (int i = 0; i < kKBlocks / 2; ++i) {
-    const int blk = wi * (kKBlocks / 2) + i;   // swizzle phase depends on i only
-    if (with_k)
-      dma16b(rk, k_lane_off<D>(i * kRpb, lane), (32 * kb) * Cfg<D>::kRowBytes + blk * 1024,
-             buf + blk * 1024);
-  }
+  // K: this wave's blocks wi*kKB .. of the half (the swizzle phase depends on
+  // i only); source and LDS both advance 1 KB per block
+  constexpr int kKB = kKBlocks / 2;
+  static_assert(kKB <= 4, "immediate offsets reach 3 KB");
+  const int kb0 = wi * kKB * 1024;
+  if (with_k)
+    static_for<kKB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma16b_imm<i * 1024>(rk, k_lane_off<D>(i * kRpb, lane),
+                           (32 * kb) * Cfg<D>::kRowBytes + kb0, buf + kb0);
+    });
 #pragma unroll
   for (int i = 0; i < kVBlocks / 2; ++i) {
     const int blk = wi * (kVBlocks / 2) + i;
