@@ -374,8 +374,8 @@ PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 MFMA (the skim tier's score produc
 
 def skim_tier(w, sh, dev, stream, reps, q_t, k_t, v_t, rp, ci, nnz, ws, o_t, attn_ms, kv_chunk):
     """The low-precision tier at the workload's size, outside the step: the
-    MXFP4 encoding of Q and K, and the tiered attention call with half and with
-    all kept pairs skimmed (tiers drawn i.i.d.).  Its bound mixes two peaks:
+    MXFP4 encoding of Q and K, and the tiered attention call with 0, 1/4, 1/2,
+    3/4 and all of the kept pairs skimmed (tiers drawn i.i.d.).  Its bound mixes two peaks:
     a skim pair's Q.K^T (2*64*64*D flops) at the FP4 rate, everything else
     (its P.V, both products of a refine pair) at the bf16 rate."""
     import numpy as np
@@ -404,7 +404,7 @@ def skim_tier(w, sh, dev, stream, reps, q_t, k_t, v_t, rp, ci, nnz, ws, o_t, att
     out = {"quantize_qk": {"us": round(q_ms * 1e3, 2), "hbm_bytes": int(moved),
                            "GB/s": round(moved / (q_ms * 1e-3) / 1e9, 1)}}
     pair = 2.0 * 64 * 64 * w.D  # flops of one product of one kept pair
-    for p_skim in (0.5, 1.0):
+    for p_skim in (0.0, 0.25, 0.5, 0.75, 1.0):
         tier = torch.from_numpy(wl.tiers(w, nnz, p_skim)).to(dev)
         n_skim = int(tier.sum().item())
         ms = timed(lambda: vsa.attn_fwd_tiered(q_t, k_t, v_t, q4, k4, rp, ci, tier, sh, w.scale,

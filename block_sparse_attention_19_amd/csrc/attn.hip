@@ -1084,6 +1084,20 @@ __device__ __forceinline__ int tier2(const SkimRef& sk, int i) {
   return (sk.t0[i] != 0 ? 1 : 0) | (sk.t1[i] != 0 ? 2 : 0);
 }
 
+// The tier bytes a step reads ahead are loaded at an index clamped into the
+// unit's list and decoded only after the step: a load under a branch whose
+// value is decoded inside it would be waited on at once, a global-memory
+// latency before the step's copies are even issued.
+struct TierBytes {
+  int b0, b1;
+};
+__device__ __forceinline__ TierBytes tier_load(const SkimRef& sk, int i) {
+  return {sk.t0[i], sk.t1[i]};
+}
+__device__ __forceinline__ int tier_bits(TierBytes t) {
+  return (t.b0 != 0 ? 1 : 0) | (t.b1 != 0 ? 2 : 0);
+}
+
 // One key tile of a G unit from LDS buffer CUR; the next tile is copied into
 // the other buffer by DMA while this one is computed on.  Both halves' score
 // MFMAs are issued before the first softmax so they run under its VALU work.
@@ -1162,27 +1176,27 @@ __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const 
     int jnn_v = (step + 2 < nkeys) ? cols[step + 2] : -1;
     int cn_v = (jn >= 0) ? a.ext[jn] : 0;
     int ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
-    int tnn_v = 0;
-    if constexpr (TIER) tnn_v = (step + 2 < nkeys) ? tier2(sk, step + 2) : 0;
+    TierBytes tb{0, 0};
+    if constexpr (TIER) tb = tier_load(sk, min(step + 2, nkeys - 1));
     g_step<D, 0, TIER, TOKR>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp,
                              TOKR ? window_dist(cc, qc) : 0);
     code = uni(cn_v);
     cc = uni(ccn_v);
     jn = uni(jnn_v);
     tc = tn;
-    tn = uni(tnn_v);
+    if constexpr (TIER) tn = (step + 2 < nkeys) ? uni(tier_bits(tb)) : 0;
     if (step + 1 >= nkeys) break;
     jnn_v = (step + 3 < nkeys) ? cols[step + 3] : -1;
     cn_v = (jn >= 0) ? a.ext[jn] : 0;
     ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
-    if constexpr (TIER) tnn_v = (step + 3 < nkeys) ? tier2(sk, step + 3) : 0;
+    if constexpr (TIER) tb = tier_load(sk, min(step + 3, nkeys - 1));
     g_step<D, 1, TIER, TOKR>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp,
                              TOKR ? window_dist(cc, qc) : 0);
     code = uni(cn_v);
     cc = uni(ccn_v);
     jn = uni(jnn_v);
     tc = tn;
-    tn = uni(tnn_v);
+    if constexpr (TIER) tn = (step + 3 < nkeys) ? uni(tier_bits(tb)) : 0;
   }
 }
 
@@ -1278,8 +1292,8 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;
     const int cn_v = (jn >= 0) ? a.ext[jn] : 0;
     const int ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
-    int tnn_v = 0;
-    if constexpr (TIER) tnn_v = (pnn < nkeys) ? (sk.t0[pnn] != 0 ? 1 : 0) : 0;
+    int tb = 0;  // raw tier byte two tiles ahead (clamped index, decoded after the step)
+    if constexpr (TIER) tb = sk.t0[min(pnn, nkeys - 1)];
     const TileExtent ext = unpack_extent(code);
     const int dist = TOKR ? window_dist(cc, qc) : 0;
     if (j >= 0) {
@@ -1301,7 +1315,8 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     cc = uni(ccn_v);
     jn = uni(jnn_v);
     t = tn;
-    tn = uni(tnn_v);
+    if constexpr (TIER) tn = (pnn < nkeys && tb != 0) ? 1 : 0;
+    tn = uni(tn);
   }
 }
 
