@@ -372,12 +372,14 @@ def configs_leg(stream, cold_reps, flush):
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 MFMA (the skim tier's score products)
 
 
-def skim_tier(w, sh, dev, stream, reps, q_t, k_t, v_t, rp, ci, nnz, ws, o_t, attn_ms, kv_chunk):
+def skim_tier(w, sh, dev, stream, reps, q_t, k_t, v_t, rp, ci, nnz, ws, o_t, kv_chunk):
     """The low-precision tier at the workload's size, outside the step: the
     MXFP4 encoding of Q and K, and the tiered attention call with 0, 1/4, 1/2,
-    3/4 and all of the kept pairs skimmed (tiers drawn i.i.d.).  Its bound mixes two peaks:
-    a skim pair's Q.K^T (2*64*64*D flops) at the FP4 rate, everything else
-    (its P.V, both products of a refine pair) at the bf16 rate."""
+    3/4 and all of the kept pairs skimmed, tiers drawn i.i.d. per pair and
+    (1/4, 1/2, 3/4) per key tile.  Each speedup is over the bf16 call on the
+    same CSR, timed in this leg.  Its bound mixes two peaks: a skim pair's
+    Q.K^T (2*64*64*D flops) at the FP4 rate, everything else (its P.V, both
+    products of a refine pair) at the bf16 rate."""
     import numpy as np
     import torch
 
@@ -404,18 +406,25 @@ def skim_tier(w, sh, dev, stream, reps, q_t, k_t, v_t, rp, ci, nnz, ws, o_t, att
     out = {"quantize_qk": {"us": round(q_ms * 1e3, 2), "hbm_bytes": int(moved),
                            "GB/s": round(moved / (q_ms * 1e-3) / 1e9, 1)}}
     pair = 2.0 * 64 * 64 * w.D  # flops of one product of one kept pair
-    for p_skim in (0.0, 0.25, 0.5, 0.75, 1.0):
-        tier = torch.from_numpy(wl.tiers(w, nnz, p_skim)).to(dev)
+    bf16_ms = timed(lambda: vsa.attn_fwd(q_t, k_t, v_t, rp, ci, sh, w.scale, kv_chunk, out=o_t,
+                                         workspace=ws, with_lse=False))
+    out["bf16_call_ms"] = round(bf16_ms, 4)
+    rp_h, ci_h = rp.cpu().numpy(), ci[:nnz].cpu().numpy()
+    recipes = [("", p, lambda p: wl.tiers(w, nnz, p)) for p in (0.0, 0.25, 0.5, 0.75, 1.0)]
+    recipes += [("_by_key_tile", p, lambda p: wl.tiers_by_key_tile(w, rp_h, ci_h, p))
+                for p in (0.25, 0.5, 0.75)]
+    for tag, p_skim, draw in recipes:
+        tier = torch.from_numpy(draw(p_skim)).to(dev)
         n_skim = int(tier.sum().item())
         ms = timed(lambda: vsa.attn_fwd_tiered(q_t, k_t, v_t, q4, k4, rp, ci, tier, sh, w.scale,
                                                kv_chunk, out=o_t, workspace=ws, with_lse=False))
         bound_ms = ((2 * nnz - n_skim) * pair / (PEAK_BF16_TFLOPS * 1e12) +
                     n_skim * pair / (PEAK_FP4_TFLOPS * 1e12)) * 1e3
-        out[f"attn_tiered_p{p_skim}"] = {
+        out[f"attn_tiered_p{p_skim}{tag}"] = {
             "skim_pairs": n_skim, "ms": round(ms, 4),
             "TFLOP/s": round(2 * nnz * pair / (ms * 1e-3) / 1e12, 2),
             "mixed_peak_ms": round(bound_ms, 4), "frac": round(bound_ms / ms, 4),
-            "speedup_vs_bf16_call": round(attn_ms / ms, 3)}
+            "speedup_vs_bf16_call": round(bf16_ms / ms, 3)}
     return out
 
 
@@ -581,7 +590,7 @@ def main():
         line["token_windows"] = token_windows(w, sh, dev, stream, args.steps, q_t, k_t, v_t, ws,
                                               o_t, args.kv_chunk, kcount)
         line["skim_tier"] = skim_tier(w, sh, dev, stream, args.steps, q_t, k_t, v_t, mbuf[0],
-                                      mbuf[1], nnz, ws, o_t, ms_attn_tiled, args.kv_chunk)
+                                      mbuf[1], nnz, ws, o_t, args.kv_chunk)
     del q_t, o_t, lse
     if not args.no_configs:
         line["configs"] = configs_leg(stream, args.cold_reps, flush)

@@ -1325,8 +1325,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_unit;
   __shared__ int s_head_done;  // this workgroup found the head of the order empty
-  const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
-  const int q = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, wave = uni(tid >> 6), lane_top = tid & 63;
   const int nT = args.nT;
   const int n_units = args.hdr->n_units;
   const int n_head = args.hdr->n_head;
@@ -1368,6 +1367,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
     const int ui = uni(s_unit);
     lds_barrier();
     if (ui < 0) break;
+    // The lane index is made opaque once per unit, so that the lane offsets
+    // the unit's set-up derives from it are recomputed per unit rather than
+    // hoisted out of the unit loop and held in registers across every step
+    // (they spilled to scratch in the tiered instance).
+    int lane = lane_top;
+    asm volatile("" : "+v"(lane));
+    const int q = lane & 31, h = lane >> 5;
     Unit u = args.units[ui];
     u.row[0] = uni(u.row[0]);
     u.row[1] = uni(u.row[1]);

@@ -166,6 +166,26 @@ def test_attention_tiered_full_small(T, H, W, heads, D, rset, kcount, p):
     assert d.max() <= LSE_ABS
 
 
+@pytest.mark.parametrize("kcount,p", [(60, 0.5), (5, 0.75)])
+def test_attention_tiered_by_key_tile(kcount, p):
+    """Tiers drawn per key tile: both rows of a pair unit agree on every tile,
+    so most tiles take the all-skim or all-refine path of the pair step."""
+    T, H, W, heads, D = 13, 9, 17, 2, 128
+    say(f"tiered by key tile T={T} H={H} W={W} heads={heads} D={D} k={kcount} p_skim={p}")
+    w = wl.custom(T, H, W, heads, D, radius_set=(1, 2, 3, 4), cid=421)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    sh, q_t, k_t, v_t, rp, ci = _prepare(w, q, k, v, r, s, kcount)
+    nnz = int(rp[-1].item())
+    tier = wl.tiers_by_key_tile(w, rp.cpu().numpy(), ci.cpu().numpy(), p)
+    assert 0 < tier.sum() < nnz
+    o, _, _ = _tiered(w, sh, q_t, k_t, v_t, rp, ci, tier)
+    keep, skim, _ = _oracle_skim(w, r, s, kcount, tier)
+    O, _ = _oracle_tiered(w, q, k, v, keep, skim)
+    got = f64_of(o)[0]
+    assert_close(np.stack([got[:, h] for h in range(heads)]), np.stack(O), "O tiered by key tile")
+
+
 def test_attention_tiered_batch2():
     """Two batch entries with different inputs, radii, scores and tiers."""
     T, H, W, heads, D = 9, 10, 11, 2, 128

@@ -186,3 +186,34 @@ def test_csr_tiers_to_tiles():
     got = vo.csr_tiers_to_tiles(row_ptr, col, tier, 3, 4)
     want = np.array([[0, 1, 0, 0], [0, 0, 0, 0], [0, 0, 1, 1]], dtype=bool)
     np.testing.assert_array_equal(got, want)
+
+
+def test_tier_recipes():
+    """Both tier recipes give one byte per CSR entry at about the asked
+    fraction; the per-key-tile one gives every pair of a (batch-head, key
+    tile) the same tier, the i.i.d. one does not."""
+    import workloads as wl
+    w = wl.custom(6, 8, 8, 3, 64, radius_set=(1, 2), cid=430)
+    nT = w.n_cells
+    rng = np.random.default_rng(3)
+    counts = rng.integers(1, nT + 1, size=w.heads * nT)
+    rp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ci = np.concatenate([np.sort(rng.choice(nT, c, replace=False)) for c in counts]).astype(np.int32)
+    nnz = int(rp[-1])
+    bh = np.repeat(np.arange(w.heads * nT) // nT, counts)
+    for p in (0.0, 0.25, 0.5, 1.0):
+        by_key = wl.tiers_by_key_tile(w, rp, ci, p)
+        iid = wl.tiers(w, nnz, p)
+        assert by_key.dtype == np.uint8 and by_key.shape == (nnz,) and iid.shape == (nnz,)
+        assert set(np.unique(by_key)) <= {0, 1} and set(np.unique(iid)) <= {0, 1}
+        key = bh * nT + ci
+        for kk in np.unique(key):
+            assert np.unique(by_key[key == kk]).size == 1
+        if p in (0.0, 1.0):
+            assert np.all(by_key == int(p)) and np.all(iid == int(p))
+        else:
+            assert abs(iid.mean() - p) < 0.03
+            # the key tiles' draws: heads * nT of them
+            u_mean = np.mean([by_key[key == kk][0] for kk in np.unique(key)])
+            assert abs(u_mean - p) < 0.1
+            assert any(np.unique(iid[key == kk]).size == 2 for kk in np.unique(key))

@@ -23,7 +23,9 @@ order or in chunks):
 * stream 3: V ~ N(0, 1);
 * stream 4: one radius per cell, discrete-uniform over the config's set;
 * stream 5: one routing score per cell, U[0, 1) drawn in float64, stored float32;
-* streams 6 / 7: per-token key budgets and routing scores (``token_inputs``).
+* streams 6 / 7: per-token key budgets and routing scores (``token_inputs``);
+* streams 8 / 9: skim tiers, per kept pair or per key tile (``tiers``,
+  ``tiers_by_key_tile``).
 
 Q/K/V are drawn in float32 and rounded to bfloat16 (round to nearest even);
 they are returned as uint16 bit patterns, token-raster order
@@ -180,6 +182,23 @@ def token_inputs(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
 def tiers(w: Workload, nnz: int, p_skim: float = 0.5) -> np.ndarray:
     """uint8 [nnz]: 1 = skim, 0 = refine."""
     return (_rng(w, 8, 0).random(nnz) < p_skim).astype(np.uint8)
+
+
+# A second recipe: the router's decision for a pair taken from statistics of
+# its key tile alone (say, the error of that tile's 4-bit K), so every query
+# tile of a head gives one key tile the same tier.  Stream 9 draws one U[0, 1)
+# per (batch-head, key tile); a pair skims if its key tile's draw is below
+# p_skim.  I.i.d. tiers are the other extreme: two query tiles agree on a key
+# tile only by chance.
+def tiers_by_key_tile(w: Workload, row_ptr: np.ndarray, col_idx: np.ndarray,
+                      p_skim: float = 0.5) -> np.ndarray:
+    """uint8 [nnz] in CSR order (rows are batch-head-major query tiles)."""
+    nT = w.n_cells
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    nnz = int(rp[-1])
+    u = _rng(w, 9, 0).random((rp.size - 1) // nT * nT)
+    bh = np.repeat(np.arange(rp.size - 1) // nT, np.diff(rp))
+    return (u[bh * nT + np.asarray(col_idx[:nnz], dtype=np.int64)] < p_skim).astype(np.uint8)
 
 
 def qkv(w: Workload, heads: Optional[range] = None):
