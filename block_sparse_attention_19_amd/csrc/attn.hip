@@ -728,6 +728,15 @@ __device__ __forceinline__ void static_for_impl(F&& f) {
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 
+// Element i of an array that no kernel writes while this one runs (the CSR,
+// the plan's tables), read through the constant address space: for a
+// wave-uniform index the compiler then issues a scalar load (counted by
+// lgkmcnt, not by the vmcnt that the tile copies use).
+template <typename T>
+__device__ __forceinline__ T ro(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 // Broadcast a wave-uniform value to a scalar register (the compiler cannot
 // prove uniformity of values derived from the thread index or read from LDS).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -1173,9 +1182,9 @@ __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const 
   wait_dma();
   lds_barrier();
   for (int step = 0; step < nkeys; step += 2) {
-    int jnn_v = (step + 2 < nkeys) ? cols[step + 2] : -1;
-    int cn_v = (jn >= 0) ? a.ext[jn] : 0;
-    int ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
+    int jnn_v = (step + 2 < nkeys) ? ro(cols, step + 2) : -1;
+    int cn_v = (jn >= 0) ? ro(a.ext, jn) : 0;
+    int ccn_v = (TOKR && jn >= 0) ? ro(a.coord, jn) : 0;
     TierBytes tb{0, 0};
     if constexpr (TIER) tb = tier_load(sk, min(step + 2, nkeys - 1));
     g_step<D, 0, TIER, TOKR>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp,
@@ -1186,9 +1195,9 @@ __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const 
     tc = tn;
     if constexpr (TIER) tn = (step + 2 < nkeys) ? uni(tier_bits(tb)) : 0;
     if (step + 1 >= nkeys) break;
-    jnn_v = (step + 3 < nkeys) ? cols[step + 3] : -1;
-    cn_v = (jn >= 0) ? a.ext[jn] : 0;
-    ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
+    jnn_v = (step + 3 < nkeys) ? ro(cols, step + 3) : -1;
+    cn_v = (jn >= 0) ? ro(a.ext, jn) : 0;
+    ccn_v = (TOKR && jn >= 0) ? ro(a.coord, jn) : 0;
     if constexpr (TIER) tb = tier_load(sk, min(step + 3, nkeys - 1));
     g_step<D, 1, TIER, TOKR>(st, smem, jn, code, tc, tn, kbase, vbase, sk, a, wave, lane, grp,
                              TOKR ? window_dist(cc, qc) : 0);
@@ -1289,9 +1298,9 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
   lds_barrier();
   for (int i = 0; i < nsteps; ++i) {
     const int pnn = 2 * (i + 2) + grp;
-    const int jnn_v = (pnn < nkeys) ? cols[pnn] : -1;
-    const int cn_v = (jn >= 0) ? a.ext[jn] : 0;
-    const int ccn_v = (TOKR && jn >= 0) ? a.coord[jn] : 0;
+    const int jnn_v = (pnn < nkeys) ? ro(cols, pnn) : -1;
+    const int cn_v = (jn >= 0) ? ro(a.ext, jn) : 0;
+    const int ccn_v = (TOKR && jn >= 0) ? ro(a.coord, jn) : 0;
     int tb = 0;  // raw tier byte two tiles ahead (clamped index, decoded after the step)
     if constexpr (TIER) tb = sk.t0[min(pnn, nkeys - 1)];
     const TileExtent ext = unpack_extent(code);
