@@ -215,19 +215,24 @@ struct PlanArgs {
   Comb* comb;
 };
 
-// Rows are taken in blocks of kPlanBlock = kPlanSeg * kPlanThreads positions
-// of the plan's order (RowOrder below).  Wave w of the block holds positions
-// 512w + 64j + lane (j < kPlanSeg): consecutive lanes write consecutive unit
+// Rows are taken in blocks of SEG * kPlanThreads positions of the plan's
+// order (RowOrder below).  Wave w of the block holds positions
+// 64 SEG w + 64j + lane (j < SEG): consecutive lanes write consecutive unit
 // records, and the order is (wave, j, lane); their row_ptr reads gather
 // within one (batch, head).  Row indices fit in 32 bits (rows * 64 tokens is
 // checked against INT_MAX on the host), so all index arithmetic here is
 // 32-bit.
-constexpr int kPlanSeg = 8;
+// SEG rows per thread: 8 for the default plan; the plan that cuts rows into
+// kv_chunk pieces places several units per row and takes 1, which keeps its
+// state in registers (at 1024 threads a lane has 128 VGPRs; at 2 rows per
+// thread it spilled 40 of them to scratch, at 8 rows 246).
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kPlanBlock = kPlanSeg * kPlanThreads;
+template <bool CHUNKED>
+constexpr int plan_seg() { return CHUNKED ? 1 : 8; }
 
+template <int SEG>
 __device__ __forceinline__ int plan_row(int c0, int j) {
-  return c0 + ((int)(threadIdx.x >> 6) << 9) + (j << 6) + (int)(threadIdx.x & 63);
+  return c0 + (int)(threadIdx.x >> 6) * (SEG * 64) + (j << 6) + (int)(threadIdx.x & 63);
 }
 
 // The order in which the plan takes the rows of one (batch, head), and so the
@@ -278,19 +283,20 @@ struct RowOrder {
 };
 
 // Lengths of this thread's rows of the block at c0 (-1 past the last row).
+template <int SEG>
 __device__ __forceinline__ void load_lengths(const int* row_ptr, int rows, int c0,
                                              const RowOrder& ord, const int* table,
-                                             int (&len)[kPlanSeg]) {
-  int a[kPlanSeg], b[kPlanSeg];
+                                             int (&len)[SEG]) {
+  int a[SEG], b[SEG];
 #pragma unroll
-  for (int j = 0; j < kPlanSeg; ++j) {
-    const int i = plan_row(c0, j);
+  for (int j = 0; j < SEG; ++j) {
+    const int i = plan_row<SEG>(c0, j);
     const int r = (i < rows) ? ord.row(i, table) : rows;
     a[j] = row_ptr[r];
     b[j] = row_ptr[min(r + 1, rows)];
   }
 #pragma unroll
-  for (int j = 0; j < kPlanSeg; ++j) len[j] = (plan_row(c0, j) < rows) ? b[j] - a[j] : -1;
+  for (int j = 0; j < SEG; ++j) len[j] = (plan_row<SEG>(c0, j) < rows) ? b[j] - a[j] : -1;
 }
 
 // Exclusive prefix of a 0/1 count over the lanes of the wave, and the wave
@@ -342,14 +348,14 @@ __device__ __forceinline__ void wave_offsets(int (&wt)[NV], int* ws, int (&total
 
 // Row-order exclusive prefix of NV per-row counts over the block (in place),
 // and the block totals; FLAGS: every count is 0 or 1.
-template <int NV, bool FLAGS>
-__device__ void block_prefix_rows(int (&v)[NV][kPlanSeg], int* ws, int (&total)[NV]) {
+template <int NV, bool FLAGS, int SEG>
+__device__ void block_prefix_rows(int (&v)[NV][SEG], int* ws, int (&total)[NV]) {
   int wt[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     int run = 0;
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) {
+    for (int j = 0; j < SEG; ++j) {
       int t;
       const int pre = FLAGS ? wave_prefix_flags(v[k][j], &t) : wave_prefix_scan(v[k][j], &t);
       v[k][j] = run + pre;
@@ -361,7 +367,7 @@ __device__ void block_prefix_rows(int (&v)[NV][kPlanSeg], int* ws, int (&total)[
 #pragma unroll
   for (int k = 0; k < NV; ++k)
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) v[k][j] += wt[k];
+    for (int j = 0; j < SEG; ++j) v[k][j] += wt[k];
 }
 
 // Thread-order exclusive prefix of NV per-thread counts (in place), and totals.
@@ -387,6 +393,8 @@ template <bool CHUNKED>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   __shared__ int ws[5 * kPlanWaves];
   __shared__ int s_chunk_g, s_sg, s_front;
+  constexpr int SEG = plan_seg<CHUNKED>();
+  constexpr int kBlock = SEG * kPlanThreads;
   const int nT = p.nT;  // >= 1
   const int t = threadIdx.x;
   const int rows = p.bh * nT;
@@ -422,21 +430,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   // pass 1: cbase[b] = complete rows before (b, h) (a scan of the complete-row
   // flags in row order), and the S totals of the incomplete rows.  With a
   // single block the lengths stay in registers for pass 2.
-  const bool one_block = rows <= kPlanBlock;
-  int len[kPlanSeg];
+  const bool one_block = rows <= kBlock;
+  int len[SEG];
   int a_units = 0, a_front = 0, a_slots = 0, a_comb = 0;
   int carry_c = 0;
-  for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
+  for (int c0 = 0; c0 < rows; c0 += kBlock) {
     load_lengths(p.row_ptr, rows, c0, ord, table, len);
-    int before[1][kPlanSeg];
+    int before[1][SEG];
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) before[0][j] = (len[j] == nT);
+    for (int j = 0; j < SEG; ++j) before[0][j] = (len[j] == nT);
     int blk[1];
     block_prefix_rows<1, true>(before, ws, blk);
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) {
+    for (int j = 0; j < SEG; ++j) {
       if (len[j] < 0) continue;
-      const int i = plan_row(c0, j);  // iteration index; its row is in (b, h) = i / nT
+      const int i = plan_row<SEG>(c0, j);  // iteration index; its row is in (b, h) = i / nT
       const int b = i / nT;
       if (i == b * nT) p.cbase[b] = carry_c + before[0][j];
       if (len[j] != nT) {
@@ -528,23 +536,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
   // pass 2: place every row
   int carry_rest = 0, carry_slot = 0, carry_comb = 0;
   carry_c = 0;
-  for (int c0 = 0; c0 < rows; c0 += kPlanBlock) {
+  for (int c0 = 0; c0 < rows; c0 += kBlock) {
     if (!one_block) load_lengths(p.row_ptr, rows, c0, ord, table, len);
-    int before[1][kPlanSeg];
+    int before[1][SEG];
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) before[0][j] = (len[j] == nT);
+    for (int j = 0; j < SEG; ++j) before[0][j] = (len[j] == nT);
     int blk_c[1];
     block_prefix_rows<1, true>(before, ws, blk_c);
     // per row: rest-region units, then (CHUNKED) partial slots and combine entries
     constexpr int NC = CHUNKED ? 3 : 1;
-    int nS[kPlanSeg];            // S chunks of the row, 0 for G members and padding
-    int cnt[NC][kPlanSeg];
+    int nS[SEG];            // S chunks of the row, 0 for G members and padding
+    int cnt[NC][SEG];
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) {
+    for (int j = 0; j < SEG; ++j) {
       nS[j] = 0;
 #pragma unroll
       for (int k = 0; k < NC; ++k) cnt[k][j] = 0;
-      const int i = plan_row(c0, j);
+      const int i = plan_row<SEG>(c0, j);
       const int b = min(i, rows - 1) / nT;
       const int cb_r = p.cbase[b], cnt_r = p.cbase[b + 1] - cb_r, gb_r = p.gbase[b];
       if (len[j] < 0) continue;
@@ -572,10 +580,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs p) {
     int blk[NC];
     block_prefix_rows<NC, !CHUNKED>(cnt, ws, blk);
 #pragma unroll
-    for (int j = 0; j < kPlanSeg; ++j) {
+    for (int j = 0; j < SEG; ++j) {
       const int n = nS[j];
       if (n == 0) continue;
-      const int r = ord.row(plan_row(c0, j), table);
+      const int r = ord.row(plan_row<SEG>(c0, j), table);
       int pos_rest = carry_rest + cnt[0][j];
       int slot0 = -1;
       if constexpr (CHUNKED) slot0 = gsl + carry_slot + cnt[1][j];
