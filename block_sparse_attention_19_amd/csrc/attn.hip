@@ -817,6 +817,9 @@ struct WaveState {
   i32x4 q4[D / 64];  // skim tier: MXFP4 Q fragments (B operands)
   int q4s;           // their scales, shifted so that byte 2m is fragment m's
   int rl;            // token-window instance: this lane's query radius (255: no limit)
+  int rl_raw;        // its token radius byte and its row's routed flag (0 or 1 in
+  int rl_routed;     // the low bit), loaded with the unit, decoded by window_radius
+  bool rl_inside;    // the lane's query slot holds a token of the grid
 };
 
 // This wave's Q fragments (B operands of S^T = K Q^T): row q of its 32 query
@@ -832,6 +835,14 @@ __device__ __forceinline__ void load_q(WaveState<D>& st, const uint16_t* qp) {
 #pragma unroll
     for (int t = 0; t < Cfg<D>::kKSteps; ++t) st.qreg[t] = bf16x8{};
   }
+}
+
+// Token-window instance: the lane's radius from the byte loaded with the unit.
+// Called after the unit's first tile has been waited for, so the byte's load
+// latency runs under that copy instead of ahead of it.
+template <int D>
+__device__ __forceinline__ void window_radius(WaveState<D>& st, int r_max) {
+  st.rl = (st.rl_inside && st.rl_routed == 0) ? min(st.rl_raw, r_max) : 255;
 }
 
 // Skim tier.  This wave's MXFP4 Q fragments: for k-block m (64 features), the
@@ -1189,6 +1200,7 @@ __device__ __forceinline__ void run_steps_g(WaveState<D>& st, char* smem, const 
   load_q<D>(st, qp);  // in flight with the first tile; one wait covers both
   wait_dma();
   lds_barrier();
+  if constexpr (TOKR) window_radius<D>(st, a.r_max);
   for (int step = 0; step < nkeys; step += 2) {
     int jnn_v = (step + 2 < nkeys) ? ro(cols, step + 2) : -1;
     int cn_v = (jn >= 0) ? ro(a.ext, jn) : 0;
@@ -1304,6 +1316,7 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
   load_q<D>(st, qp);  // in flight with the first half tile; one wait covers both
   wait_dma();
   lds_barrier();
+  if constexpr (TOKR) window_radius<D>(st, a.r_max);
   for (int i = 0; i < nsteps; ++i) {
     const int pnn = 2 * (i + 2) + grp;
     const int jnn_v = (pnn < nkeys) ? ro(cols, pnn) : -1;
@@ -1435,24 +1448,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs args) {
                  args.q4s + (qrow0 + q) * Cfg4<D>::kC4, h);
     }
     int qc = 0;  // packed coordinates of this wave's query tile (token-window instance)
+    bool windowed = TOKR;
     if constexpr (TOKR) {
       // this lane's query token and its own radius: 255 (no limit) for routed
-      // rows and padded slots, whose outputs are not windowed or are dropped
-      qc = uni(args.coord[row - (int)bh * nT]);
+      // rows and padded slots, whose outputs are not windowed or are dropped.
+      // The radius byte is loaded at a valid index whatever the lane and
+      // decoded after the first tile's wait (window_radius).
+      qc = ro(args.coord, row - (int)bh * nT);
       const int qs = 32 * half + q;
       const int t = 4 * (qc & 1023) + (qs >> 4);
       const int hh = 4 * ((qc >> 10) & 1023) + ((qs >> 2) & 3);
       const int w = 4 * ((qc >> 20) & 1023) + (qs & 3);
-      int rl = 255;
-      if (!uni(args.routed[row]) && t < args.T && hh < args.H && w < args.W) {
-        const int64_t n = ((int64_t)t * args.H + hh) * args.W + w;
-        rl = min((int)args.tok_r[bh * ((int64_t)args.T * args.H * args.W) + n], args.r_max);
-      }
-      st.rl = rl;
+      const bool inside = t < args.T && hh < args.H && w < args.W;
+      const int64_t n = inside ? ((int64_t)t * args.H + hh) * args.W + w : 0;
+      st.rl_raw = args.tok_r[bh * ((int64_t)args.T * args.H * args.W) + n];
+      st.rl_routed = args.routed[row];
+      st.rl_inside = inside;
+      // a pair unit of two routed rows is not windowed: it takes the plain step
+      windowed = !g_mode || !(uni(args.routed[u.row[0]]) && uni(args.routed[u.row[1]]));
     }
-    if (g_mode)
+    if (g_mode && windowed)
       run_steps_g<D, TIER, TOKR>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, qp,
                                  grp, qc);
+    else if (g_mode)
+      run_steps_g<D, TIER, false>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, qp,
+                                  grp, qc);
     else
       run_steps_s<D, TIER, TOKR>(st, smem, cols, nkeys, kbase, vbase, sk, args, wave, lane, grp,
                                  qp, qc);
