@@ -1154,18 +1154,22 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int
     }
   }
   const TileExtent ext = unpack_extent(code);
+  // Half 1 (time slices 2 and 3 of the key tile) holds only padding keys when
+  // the tile has at most 2 valid time slices: all its scores would be -inf and
+  // its probabilities exactly 0, so it is skipped.
+  const bool half1 = ext.vt > 2;
   f32x16 s0, s1;
   if (TIER && ((tc >> grp) & 1)) {
     const char* k4buf = smem + Cfg<D>::kLdsBytes + CUR * Cfg4<D>::kTileAll;
     const int row = sigma(lane & 31), h = lane >> 5;
     s0 = qk32_skim<D>(k4buf, k4buf + Cfg4<D>::kTileCodes, row, st, h);
-    s1 = qk32_skim<D>(k4buf, k4buf + Cfg4<D>::kTileCodes, 32 + row, st, h);
+    if (half1) s1 = qk32_skim<D>(k4buf, k4buf + Cfg4<D>::kTileCodes, 32 + row, st, h);
   } else {
     s0 = qk32<D>(kbuf, st, lane);
-    s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
+    if (half1) s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
   }
   softmax_pv_half<D, false, TOKR>(st, s0, vbuf, 0, lane, ext, a.c2, dist);
-  softmax_pv_half<D, false, TOKR>(st, s1, vbuf, 1, lane, ext, a.c2, dist);
+  if (half1) softmax_pv_half<D, false, TOKR>(st, s1, vbuf, 1, lane, ext, a.c2, dist);
   wait_dma();
   lds_barrier();
 }
@@ -1334,7 +1338,9 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     wait_dma();
     lds_barrier();
     if (jn >= 0) fetch(jn, tn, 0, 0);
-    if (j >= 0) {
+    // half 1 of a tile with at most 2 valid time slices holds only padding
+    // keys (scores -inf, probabilities exactly 0): skipped
+    if (j >= 0 && ext.vt > 2) {
       const f32x16 s1 = scores(t, 1);
       softmax_pv_half<D, true, TOKR>(st, s1, region + BUF + KH, 1, lane, ext, a.c2, dist);
     }

@@ -220,9 +220,10 @@ size_t vsa_attn_workspace_bytes(const vsa_shape* s, int32_t kv_chunk);
  *            kv_chunk); its contents need no initialisation.
  * Padding keys (slots outside the grid) are excluded from every softmax by
  * position: their K values never matter, and their V values are multiplied
- * by a probability of exactly 0, so they must be finite (the permute writes
- * +0.0 there); a NaN or infinity in a padded V slot makes the outputs of the
- * query tiles that list that key tile NaN.
+ * by a probability of exactly 0 (or, for the 32 keys of time slices 2-3 of a
+ * key tile with at most 2 valid time slices, not read at all), so they must
+ * be finite (the permute writes +0.0 there); a NaN or infinity in a padded V
+ * slot may make the outputs of the query tiles that list that key tile NaN.
  * Errors: INVALID_ARG, UNSUPPORTED (head_dim not 64/128), CAPACITY (ws),
  * OVERFLOW.
  */
