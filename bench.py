@@ -15,7 +15,9 @@ head_dim 128, radii in {1, 2, 3}, 20% of query tiles routed dense.
 Prints ONE JSON line.  ``value`` is retained-tile bf16 TFLOP/s of the whole
 step (kept tile pairs x 4*64*64*D flops over the step time); ``roofline``
 rates the attention kernel alone against the bf16 MFMA peak; ``cpu_baseline``
-times the fp64 CPU oracle on a bounded sample of the same workload;
+times the fp64 CPU oracle on a bounded sample of the same workload, and
+``parity`` compares the oracle rows of that sample with the step's output
+(max |dO|, sum |dO| / sum |O|, worst row relative L2, max |dLSE|);
 ``token_level_calls`` times the per-token -> per-tile calls (budget -> radius,
 tile radius, tile score) and ``skim_tier`` the MXFP4 encoding and the tiered
 attention call (half / all kept pairs skimmed) at the workload's size, both
@@ -119,9 +121,19 @@ def traffic_figure(n_launch_units: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, r, s, kcount, budget_s):
+# Output tolerance of the bf16-in / fp32-accumulate path against the fp64
+# oracle (the same bounds the GPU parity tests assert): max |dO|, sum |dO| /
+# sum |O|, and max |dLSE| (natural log).
+PARITY_MAX_ABS, PARITY_MEAN_REL, PARITY_LSE_ABS = 2e-2, 3e-3, 2e-3
+
+
+def cpu_baseline(w, q, k, v, r, s, kcount, budget_s, o_gpu=None, lse_gpu=None):
     """fp64 oracle on sampled query tiles of the same workload, until the time
-    budget is spent; rated in retained-tile TFLOP/s like the GPU."""
+    budget is spent; rated in retained-tile TFLOP/s like the GPU.
+
+    With the step's GPU output (raster O [1, N, Hh, D] bf16 and LSE [1, Hh, N]
+    fp32, host copies), the oracle rows computed for the timing are compared
+    with it afterwards, outside the timed loop: returns (baseline, parity)."""
     import numpy as np
     from oracle import vsa_oracle as vo
     # the host cores this process may run on; numpy's BLAS (the oracle's
@@ -135,23 +147,60 @@ def cpu_baseline(w, q, k, v, r, s, kcount, budget_s):
     rng = np.random.default_rng(1234)
     tt = vo.token_tile(w.T, w.H, w.W)
     done_tiles, pairs, t0 = 0, 0, time.perf_counter()
+    kept = []  # (head, tile, routed, rows, oracle O, oracle LSE) for the parity check
     while time.perf_counter() - t0 < budget_s:
         h = int(rng.integers(w.heads))
-        keep = vo.tile_keep(r[0, h], vo.routed_tiles(s[0, h], kcount), w.T, w.H, w.W)
+        routed = vo.routed_tiles(s[0, h], kcount)
+        keep = vo.tile_keep(r[0, h], routed, w.T, w.H, w.W)
         qf, kf, vf = (vo.bf16_to_f64(x[0, :, h]) for x in (q, k, v))
         for a in rng.permutation(w.n_cells)[:8]:
             rows = np.flatnonzero(tt == a)
-            vo.attention_head_rows(qf, kf, vf, keep, tt, rows, w.scale)
+            ref_o, ref_lse = vo.attention_head_rows(qf, kf, vf, keep, tt, rows, w.scale)
             done_tiles += 1
             pairs += int(keep[a].sum())
+            kept.append((h, int(a), bool(routed[a]), rows, ref_o, ref_lse))
     el = time.perf_counter() - t0
     if limiter is not None:
         limiter.unregister()
     flops = pairs * 4.0 * 64 * 64 * w.D
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    base = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done_tiles} query tiles ({pairs} retained tile pairs) of {w.name}, "
                       f"fp64 masked attention over all keys, {el:.1f} s; full-call "
                       f"extrapolation {el / max(done_tiles, 1) * w.heads * w.n_cells:.0f} s"}
+    if o_gpu is None or not kept:
+        return base, None
+    # parity of the sampled rows: the step's bf16 O and fp32 LSE against the oracle
+    got_o = o_gpu[0].float().numpy()       # [N, Hh, D], exact bf16 values
+    got_lse = lse_gpu[0].numpy()           # [Hh, N]
+    c = vo.tile_coords(w.T, w.H, w.W)
+    edge = (4 * (c[:, 0] + 1) > w.T) | (4 * (c[:, 1] + 1) > w.H) | (4 * (c[:, 2] + 1) > w.W)
+    max_abs, sum_d, sum_ref, row_l2, lse_abs, n_rows = 0.0, 0.0, 0.0, 0.0, 0.0, 0
+    finite = True
+    for h, a, _, rows, ref_o, ref_lse in kept:
+        g = got_o[rows, h].astype(np.float64)
+        d = np.abs(g - ref_o)
+        finite &= bool(np.all(np.isfinite(g)))
+        max_abs = max(max_abs, float(d.max()))
+        sum_d += float(d.sum())
+        sum_ref += float(np.abs(ref_o).sum())
+        row_l2 = max(row_l2, float((np.linalg.norm(g - ref_o, axis=1) /
+                                    np.linalg.norm(ref_o, axis=1)).max()))
+        lse_abs = max(lse_abs, float(np.abs(got_lse[h, rows].astype(np.float64) - ref_lse).max()))
+        n_rows += len(rows)
+    mean_rel = sum_d / max(sum_ref, 1e-300)
+    parity = {
+        "against": "fp64 oracle (masked softmax over every key of the head)",
+        "tiles": len(kept), "distinct_tiles": len({(x[0], x[1]) for x in kept}),
+        "routed_tiles": sum(1 for x in kept if x[2]),
+        "edge_tiles": sum(1 for x in kept if edge[x[1]]), "rows": n_rows,
+        "heads": sorted({x[0] for x in kept}),
+        "max_abs": max_abs, "mean_rel": mean_rel, "row_rel_l2_max": row_l2, "lse_max_abs": lse_abs,
+        "tolerance": {"max_abs": PARITY_MAX_ABS, "mean_rel": PARITY_MEAN_REL,
+                      "lse_max_abs": PARITY_LSE_ABS},
+        "pass": bool(finite and max_abs <= PARITY_MAX_ABS and mean_rel <= PARITY_MEAN_REL
+                     and lse_abs <= PARITY_LSE_ABS),
+    }
+    return base, parity
 
 
 def token_level_calls(w, sh, dev, stream, reps):
@@ -538,6 +587,10 @@ def main():
                                                           lse_out=lse_r),
                               stream, args.cold_reps, flush=flush)
     cold_step = time_launches(step, stream, args.cold_reps, flush=flush)
+    # the step's output (raster O and LSE of the last step), for the parity
+    # check of the oracle leg
+    torch.cuda.synchronize()
+    o_host, lse_host = o.cpu(), lse_r.cpu()
     nnz = int(mbuf[0][-1].item())
     flops = nnz * 4.0 * 64 * 64 * w.D
     # valid-token flops: each kept pair weighted by valid queries x valid keys
@@ -595,7 +648,8 @@ def main():
     if not args.no_configs:
         line["configs"] = configs_leg(stream, args.cold_reps, flush)
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, r, s, kcount, args.cpu_seconds)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(w, q, k, v, r, s, kcount,
+                                                            args.cpu_seconds, o_host, lse_host)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
