@@ -891,7 +891,9 @@ __device__ __forceinline__ f32x16 qk32_skim(const char* k4buf, const char* sc, i
 
 // S^T (32 keys x 32 queries) = K Q^T for this wave's 32 query rows, from a
 // block of 32 consecutive K rows (`k32`: row i of the block at i * 2D bytes,
-// swizzled as k_off).
+// swizzled as k_off).  All the K operands are read before the first MFMA (a
+// scheduling barrier keeps them there), so the chain waits on the LDS once,
+// not once per k-step as when the compiler issues each read at its MFMA.
 template <int D>
 __device__ __forceinline__ f32x16 qk32(const char* k32, const WaveState<D>& st, int lane) {
   const int q = lane & 31, h = lane >> 5;
@@ -899,11 +901,14 @@ __device__ __forceinline__ f32x16 qk32(const char* k32, const WaveState<D>& st, 
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  bf16x8 a[Cfg<D>::kKSteps];
 #pragma unroll
-  for (int t = 0; t < Cfg<D>::kKSteps; ++t) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(k32 + k_off<D>(krow, 2 * t + h));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[t], s, 0, 0, 0);
-  }
+  for (int t = 0; t < Cfg<D>::kKSteps; ++t)
+    a[t] = *reinterpret_cast<const bf16x8*>(k32 + k_off<D>(krow, 2 * t + h));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < Cfg<D>::kKSteps; ++t)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], st.qreg[t], s, 0, 0, 0);
   return s;
 }
 
