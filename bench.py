@@ -590,7 +590,7 @@ def main():
     # the step's output (raster O and LSE of the last step), for the parity
     # check of the oracle leg
     torch.cuda.synchronize()
-    o_host, lse_host = o.cpu(), lse_r.cpu()
+    o_host, lse_host = (o.cpu(), lse_r.cpu()) if args.cpu_seconds > 0 else (None, None)
     nnz = int(mbuf[0][-1].item())
     flops = nnz * 4.0 * 64 * 64 * w.D
     # valid-token flops: each kept pair weighted by valid queries x valid keys
