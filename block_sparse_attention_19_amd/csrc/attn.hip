@@ -934,12 +934,13 @@ __device__ __forceinline__ float sum_halves(float x) {
 // i.e. lt = 2kb + r/8, lh = 2h + (r/4)%2, lw = r%4.
 // HALF_V: `vbuf` holds only the 32 keys of this half ([D][32], vh_off);
 // otherwise the whole tile ([D][64], v_off).
-// EARLY_V: the P.V operands are read from LDS before the softmax, so that the
-// reads' latency runs under its VALU work; left to itself the compiler issues
-// each read just before its MFMA and waits for it there.  It holds 8 more
-// registers per D-block through the softmax (the skim instance, already near
-// the register limit, reads them late).
-template <int D, bool HALF_V, bool TOKR = false, bool EARLY_V = false>
+// EARLY_V: how many of the half's 2 * D/32 P.V operands are read from LDS
+// before the softmax, so that the reads' latency runs under its VALU work;
+// left to itself the compiler issues each read just before its MFMA and waits
+// for it there.  Each one holds 4 registers through the softmax: the skim
+// instance, near the register limit in its pair steps, reads three quarters
+// of them early there.
+template <int D, bool HALF_V, bool TOKR = false, int EARLY_V = 0>
 __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, const char* vbuf,
                                                 int kb, int lane, const TileExtent& ext,
                                                 float c2, int dist = 0) {
@@ -948,12 +949,14 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
     const int voff = HALF_V ? vh_off(32 * db + q, 2 * s2 + h) : v_off(32 * db + q, 4 * kb + 2 * s2 + h);
     return *reinterpret_cast<const bf16x8*>(vbuf + voff);
   };
+  static_assert(EARLY_V >= 0 && EARLY_V <= 2 * Cfg<D>::kDBlocks, "early operand count");
   bf16x8 vf[2 * Cfg<D>::kDBlocks];
-  if constexpr (EARLY_V) {
+  if constexpr (EARLY_V > 0) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int db = 0; db < Cfg<D>::kDBlocks; ++db) vf[s2 * Cfg<D>::kDBlocks + db] = v_frag(s2, db);
+      for (int db = 0; db < Cfg<D>::kDBlocks; ++db)
+        if (s2 * Cfg<D>::kDBlocks + db < EARLY_V) vf[s2 * Cfg<D>::kDBlocks + db] = v_frag(s2, db);
     // keeps the scheduler from sinking each read back to its MFMA
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1014,7 +1017,8 @@ __device__ __forceinline__ void softmax_pv_half(WaveState<D>& st, f32x16 s, cons
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int db = 0; db < Cfg<D>::kDBlocks; ++db) {
-      const bf16x8 a = EARLY_V ? vf[s2 * Cfg<D>::kDBlocks + db] : v_frag(s2, db);
+      const bf16x8 a = (s2 * Cfg<D>::kDBlocks + db < EARLY_V) ? vf[s2 * Cfg<D>::kDBlocks + db]
+                                                              : v_frag(s2, db);
       st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], st.o[db], 0, 0, 0);
     }
 }
@@ -1190,8 +1194,9 @@ __device__ __forceinline__ void g_step(WaveState<D>& st, char* smem, int jn, int
     s0 = qk32<D>(kbuf, st, lane);
     if (half1) s1 = qk32<D>(kbuf + 32 * Cfg<D>::kRowBytes, st, lane);
   }
-  softmax_pv_half<D, false, TOKR, !TIER>(st, s0, vbuf, 0, lane, ext, a.c2, dist);
-  if (half1) softmax_pv_half<D, false, TOKR, !TIER>(st, s1, vbuf, 1, lane, ext, a.c2, dist);
+  constexpr int kEarlyV = TIER ? 3 * Cfg<D>::kDBlocks / 2 : 2 * Cfg<D>::kDBlocks;
+  softmax_pv_half<D, false, TOKR, kEarlyV>(st, s0, vbuf, 0, lane, ext, a.c2, dist);
+  if (half1) softmax_pv_half<D, false, TOKR, kEarlyV>(st, s1, vbuf, 1, lane, ext, a.c2, dist);
   wait_dma();
   lds_barrier();
 }
@@ -1355,7 +1360,7 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     if (j >= 0) {
       fetch(j, t, 1, 1);
       const f32x16 s0 = scores(t, 0);
-      softmax_pv_half<D, true, TOKR, !TIER>(st, s0, region + KH, 0, lane, ext, a.c2, dist);
+      softmax_pv_half<D, true, TOKR, 2 * Cfg<D>::kDBlocks>(st, s0, region + KH, 0, lane, ext, a.c2, dist);
     }
     wait_dma();
     lds_barrier();
@@ -1364,7 +1369,8 @@ __device__ __forceinline__ void run_steps_s(WaveState<D>& st, char* smem, const 
     // keys (scores -inf, probabilities exactly 0): skipped
     if (j >= 0 && ext.vt > 2) {
       const f32x16 s1 = scores(t, 1);
-      softmax_pv_half<D, true, TOKR, !TIER>(st, s1, region + BUF + KH, 1, lane, ext, a.c2, dist);
+      softmax_pv_half<D, true, TOKR, 2 * Cfg<D>::kDBlocks>(st, s1, region + BUF + KH, 1, lane, ext,
+                                                             a.c2, dist);
     }
     wait_dma();
     lds_barrier();
