@@ -1090,9 +1090,15 @@ __device__ __forceinline__ void dma_tile(char* buf, const char* ktile, const cha
   // V^T); the swizzle phase depends on i only (w*kPer*kRpb % 16 == 0)
   static_assert(kPer <= 4, "immediate offsets reach 3 KB");
   const int b0 = w * kPer * 1024;
+  // all K blocks, then all V blocks: the copy rewrites the LDS base (M0)
+  // once per run instead of once per block
+  if (with_k)
+    static_for<kPer>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma16b_imm<i * 1024>(rk, k_lane_off<D>(i * kRpb, lane), b0, buf + b0);
+    });
   static_for<kPer>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    if (with_k) dma16b_imm<i * 1024>(rk, k_lane_off<D>(i * kRpb, lane), b0, buf + b0);
     dma16b_imm<i * 1024>(rv, v_lane_off(i * 8, lane), b0, buf + TB + b0);
   });
 }
@@ -1283,15 +1289,19 @@ __device__ __forceinline__ void dma_half(char* buf, const char* ktile, const cha
       dma16b_imm<i * 1024>(rk, k_lane_off<D>(i * kRpb, lane),
                            (32 * kb) * Cfg<D>::kRowBytes + kb0, buf + kb0);
     });
-#pragma unroll
-  for (int i = 0; i < kVBlocks / 2; ++i) {
-    const int blk = wi * (kVBlocks / 2) + i;
-    // rows d = blk*16 + lane/4 (64-byte rows of 32 keys); chunk 4kb + c4 of the
-    // global 128-byte row; the swizzle phase (d >> 2) & 3 = (lane >> 4) & 3
-    const int d = blk * 16 + (lane >> 2);
+  // V blocks: consecutive 1 KB blocks of LDS from source rows 2 KB apart; one
+  // LDS base for the run, the immediate offset moving both addresses by 1 KB
+  // per block and the scalar offset adding the source's other 1 KB
+  static_assert(kVBlocks / 2 <= 4, "immediate offsets reach 3 KB");
+  {
+    const int blk0 = wi * (kVBlocks / 2);
+    const int d = blk0 * 16 + (lane >> 2);
     const int c4 = (lane & 3) ^ ((d >> 2) & 3);
     const uint32_t off = (uint32_t)((lane >> 2) * 128 + (c4 << 4));
-    dma16b(rv, off, blk * 16 * 128 + kb * 64, buf + KH + blk * 1024);
+    static_for<kVBlocks / 2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      dma16b_imm<i * 1024>(rv, off, blk0 * 16 * 128 + kb * 64 + i * 1024, buf + KH + blk0 * 1024);
+    });
   }
 }
 
