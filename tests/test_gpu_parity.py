@@ -482,3 +482,41 @@ def test_attention_composed_fused_and_unfused():
     assert np.array_equal(bits_of(a), bits_of(b))
     ref, _ = vo.attention(q, k, v, r, s, kcount, w.T, w.H, w.W, w.scale)
     assert_close(f64_of(a), ref, "O composed")
+
+
+@pytest.mark.parametrize("D,kv_chunk", [(128, 0), (64, 0), (128, 3)])
+def test_attention_running_max_moves_every_tile(D, kv_chunk):
+    """Scores that grow with the key tile's index: a shared direction u is added
+    to every query and c(tau) * u to every key of key tile tau, with c rising by
+    10 log2 units of score per tile, so each later tile of a row lifts the
+    running maximum past the lazy-rescale slack (2^8) and the rescale branch
+    runs on almost every tile, for routed and local rows; tile-major and raster
+    calls, O and LSE against the oracle."""
+    T, H, W, heads = 9, 10, 11, 2        # 27 key tiles, ragged on every axis
+    w = wl.custom(T, H, W, heads, D, radius_set=(1, 2, 3), cid=430)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    kcount = 5
+    tt = vo.token_tile(T, H, W)
+    a = 0.5
+    c2 = w.scale / math.log(2.0)           # log2 units of score per raw unit
+    step = 10.0 / (c2 * D * a * a)          # +10 log2 units per key tile
+    qf = vo.bf16_to_f64(q) + a
+    kf = vo.bf16_to_f64(k) + (step * tt.astype(np.float64) * a)[None, :, None, None]
+    q2 = wl.f32_to_bf16_bits(qf.astype(np.float32))
+    k2 = wl.f32_to_bf16_bits(kf.astype(np.float32))
+    say(f"attention running max moves D={D} kv_chunk={kv_chunk} key bias up to {step * tt.max() * a:.1f}")
+    out = _run_all(w, q2, k2, v, r, s, kcount, kv_chunk=kv_chunk)
+    ref, lse_ref = vo.attention(q2, k2, v, r, s, kcount, T, H, W, w.scale)
+    assert_close(f64_of(out["o"]), ref, "O tile-major")
+    lse_t = out["lse"].cpu().numpy().astype(np.float64)
+    lse_ref_t = vo.permute(lse_ref.transpose(0, 2, 1)[..., None], T, H, W)[..., 0]
+    valid = vo.permute(np.ones((1, T * H * W, heads, 1)), T, H, W)[..., 0] > 0
+    d = np.abs(lse_t - lse_ref_t)[valid]
+    say(f"  LSE max_abs={d.max():.3e} (LSE up to {np.abs(lse_ref).max():.0f})")
+    assert d.max() <= LSE_ABS
+    sh = _shape(w)
+    o_r, lse_r = vsa.attn_fwd_raster(bf16_to_dev(q2), out["k_t"], out["v_t"], out["rp"], out["ci"],
+                                     sh, w.scale, kv_chunk)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(o_r), bits_of(out["o"]))
