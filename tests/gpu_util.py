@@ -1,4 +1,5 @@
-"""Helpers shared by the GPU tests (device transfer, error statistics)."""
+"""Helpers shared by the GPU tests (device transfer, error statistics, input recipes)."""
+import math
 import sys
 
 import numpy as np
@@ -43,3 +44,18 @@ def assert_close(got, ref, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert mx <= MAX_ABS, f"{what}: max_abs {mx} > {MAX_ABS}"
     assert mr <= MEAN_REL, f"{what}: mean_rel {mr} > {MEAN_REL}"
+
+
+def rising_scores(w, q, k, a=0.5, per_tile=10.0):
+    """Q and K (bf16 bits, [B, N, heads, D]) reshaped so that scores rise with
+    the key tile's index: a shared direction (every feature a) is added to every
+    query and, times c(tau), to every key of key tile tau, with c raising the
+    score by about `per_tile` log2 units per tile.  A row's running maximum then
+    passes the lazy-rescale slack on most of its tiles."""
+    import workloads as wl
+    tt = vo.token_tile(w.T, w.H, w.W)
+    c2 = w.scale / math.log(2.0)
+    step = per_tile / (c2 * w.D * a * a)
+    qf = vo.bf16_to_f64(q) + a
+    kf = vo.bf16_to_f64(k) + (step * tt.astype(np.float64) * a)[None, :, None, None]
+    return (wl.f32_to_bf16_bits(qf.astype(np.float32)), wl.f32_to_bf16_bits(kf.astype(np.float32)))

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import LSE_ABS, assert_close, bf16_to_dev, bits_of, dev, f64_of, say
+from gpu_util import LSE_ABS, assert_close, bf16_to_dev, bits_of, dev, f64_of, rising_scores, say
 from oracle import vsa_oracle as vo
 
 pytestmark = pytest.mark.gpu
@@ -497,15 +497,8 @@ def test_attention_running_max_moves_every_tile(D, kv_chunk):
     q, k, v = wl.qkv(w)
     r, s = wl.radii_scores(w)
     kcount = 5
-    tt = vo.token_tile(T, H, W)
-    a = 0.5
-    c2 = w.scale / math.log(2.0)           # log2 units of score per raw unit
-    step = 10.0 / (c2 * D * a * a)          # +10 log2 units per key tile
-    qf = vo.bf16_to_f64(q) + a
-    kf = vo.bf16_to_f64(k) + (step * tt.astype(np.float64) * a)[None, :, None, None]
-    q2 = wl.f32_to_bf16_bits(qf.astype(np.float32))
-    k2 = wl.f32_to_bf16_bits(kf.astype(np.float32))
-    say(f"attention running max moves D={D} kv_chunk={kv_chunk} key bias up to {step * tt.max() * a:.1f}")
+    q2, k2 = rising_scores(w, q, k)
+    say(f"attention running max moves D={D} kv_chunk={kv_chunk}")
     out = _run_all(w, q2, k2, v, r, s, kcount, kv_chunk=kv_chunk)
     ref, lse_ref = vo.attention(q2, k2, v, r, s, kcount, T, H, W, w.scale)
     assert_close(f64_of(out["o"]), ref, "O tile-major")

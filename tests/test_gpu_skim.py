@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import LSE_ABS, assert_close, bf16_to_dev, bits_of, dev, f64_of, say
+from gpu_util import LSE_ABS, assert_close, bf16_to_dev, bits_of, dev, f64_of, rising_scores, say
 from oracle import vsa_oracle as vo
 
 pytestmark = pytest.mark.gpu
@@ -302,3 +302,29 @@ def test_attention_tiered_arbitrary_csr():
                         torch.from_numpy(ci).to(dev()), tier)
     skim = vo.csr_tiers_to_tiles(rp, ci, tier, heads * nT, nT).reshape(heads, nT, nT)
     _check_csr_attention(w, q, k, v, rp, ci, o, lse, skim=skim)
+
+
+@pytest.mark.parametrize("D,p", [(128, 0.5), (64, 0.5)])
+def test_attention_tiered_running_max_moves_every_tile(D, p):
+    """The skim instance on scores that rise with the key tile's index (the
+    running maximum moves on most tiles of every row, skim and refine pairs
+    mixed): O and LSE against the oracle's tiered attention."""
+    T, H, W, heads, kcount = 9, 10, 11, 2, 5
+    w = wl.custom(T, H, W, heads, D, radius_set=(1, 2, 3), cid=430)
+    q, k, v = wl.qkv(w)
+    r, s = wl.radii_scores(w)
+    q, k = rising_scores(w, q, k)
+    say(f"tiered running max moves D={D} p_skim={p}")
+    sh, q_t, k_t, v_t, rp, ci = _prepare(w, q, k, v, r, s, kcount)
+    tier = wl.tiers(w, int(rp[-1].item()), p)
+    o, o_t, lse = _tiered(w, sh, q_t, k_t, v_t, rp, ci, tier)
+    keep, skim, _ = _oracle_skim(w, r, s, kcount, tier)
+    O, L = _oracle_tiered(w, q, k, v, keep, skim)
+    got = f64_of(o)[0]
+    assert_close(np.stack([got[:, h] for h in range(heads)]), np.stack(O), "O tiered")
+    lse_t = lse.cpu().numpy().astype(np.float64)[0]
+    lse_ref = vo.permute(np.stack(L).T[None, :, :, None], T, H, W)[0, ..., 0]
+    valid = vo.permute(np.ones((1, T * H * W, heads, 1)), T, H, W)[0, ..., 0] > 0
+    d = np.abs(lse_t - lse_ref)[valid]
+    say(f"  LSE max_abs={d.max():.3e}")
+    assert d.max() <= LSE_ABS

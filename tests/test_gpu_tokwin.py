@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import LSE_ABS, assert_close, bf16_to_dev, bits_of, dev, f64_of, say
+from gpu_util import LSE_ABS, assert_close, bf16_to_dev, bits_of, dev, f64_of, rising_scores, say
 from oracle import vsa_oracle as vo
 
 pytestmark = pytest.mark.gpu
@@ -136,3 +136,22 @@ def test_token_window_wan13b_sampled():
     # the windows bite: kept tiles outside some tokens' own windows
     say(f"  (token, kept tile) pairs outside the token's window: {windowed_out}")
     assert windowed_out > 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_token_window_running_max_moves_every_tile(D):
+    """Exact per-token windows on scores that rise with the key tile's index
+    (the running maximum moves on most tiles a token attends): O and LSE."""
+    T, H, W, heads = 9, 10, 11, 2
+    w = wl.custom(T, H, W, heads, D, cid=431)
+    q, k, v = wl.qkv(w)
+    _, s = wl.radii_scores(w)
+    q, k = rising_scores(w, q, k)
+    rng = np.random.default_rng(D + 7)
+    tok_r = rng.integers(0, 4, size=(1, heads, T * H * W)).astype(np.uint8)
+    for kcount in (0, 3):
+        say(f"token windows running max moves D={D} k={kcount}")
+        out = _run(w, q, k, v, tok_r, s, kcount, 3)
+        ref, lse = vo.token_window_attention(q, k, v, tok_r, s, kcount, 3, T, H, W, w.scale)
+        assert_close(f64_of(out["o"]), ref, "O")
+        _check_lse(out, lse, T, H, W, heads)
