@@ -480,7 +480,7 @@ def skim_tier(w, sh, dev, stream, reps, q_t, k_t, v_t, rp, ci, nnz, ws, o_t, kv_
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import numpy as np

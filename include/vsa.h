@@ -49,7 +49,7 @@ extern "C" {
 typedef enum vsa_status {
   VSA_OK = 0,
   VSA_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or count   */
-  VSA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement    */
+  VSA_ERR_UNSUPPORTED = 2, /* valid request the library does not implement   */
   VSA_ERR_CAPACITY = 3,    /* an output or workspace buffer is too small     */
   VSA_ERR_OVERFLOW = 4,    /* an index would not fit the int32 layouts       */
   VSA_ERR_HIP = 5          /* the HIP runtime refused a launch               */
